@@ -1,0 +1,89 @@
+"""Algorithmic work of one block forward: FLOPs, bytes and parameter counts.
+
+Used by the benchmark to turn measured times into TFLOP/s, GB/s and roofline
+fractions.  Conventions:
+  * a matrix product of [m, k] by [k, n] costs 2*m*k*n FLOPs (the "2mnp" rule
+    of "LLaMA-3 8B 现代 LLM 架构、计算规模与能耗", §八);
+  * causal attention counts only visible (query, key) pairs: QK^T and PV each
+    cost 2*hd per pair and head; the dense convention of that page (every pair
+    of an S x S matrix) is also provided for comparison;
+  * HBM bytes are the algorithmic minimum: every input read once, every output
+    written once.
+"""
+
+from dataclasses import dataclass
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+@dataclass(frozen=True)
+class Shape:
+    d_model: int
+    n_q: int
+    n_kv: int
+    head_dim: int
+    d_ff: int
+
+
+def linear_params(s):
+    """Weights of the four attention and three FFN projections."""
+    attn = s.d_model * s.n_q * s.head_dim * 2 + 2 * s.d_model * s.n_kv * s.head_dim
+    return attn + 3 * s.d_model * s.d_ff
+
+
+def block_params(s):
+    return linear_params(s) + 2 * s.d_model
+
+
+def attention_params(s):
+    return s.d_model * s.n_q * s.head_dim * 2 + 2 * s.d_model * s.n_kv * s.head_dim
+
+
+def mlp_params(s):
+    return 3 * s.d_model * s.d_ff
+
+
+def prefill_linear_flops(s, n_tokens):
+    return 2 * n_tokens * linear_params(s)
+
+
+def causal_pairs(batch, seq):
+    return batch * seq * (seq + 1) // 2
+
+
+def prefill_attention_flops(s, batch, seq):
+    return 4 * s.head_dim * s.n_q * causal_pairs(batch, seq)
+
+
+def dense_attention_flops(s, batch, seq):
+    return 4 * s.head_dim * s.n_q * batch * seq * seq
+
+
+def prefill_flops(s, batch, seq):
+    return prefill_linear_flops(s, batch * seq) + prefill_attention_flops(s, batch, seq)
+
+
+def decode_attention_flops(s, batch, attend_len):
+    return 4 * s.head_dim * s.n_q * batch * attend_len
+
+
+def decode_flops(s, batch, attend_len):
+    return prefill_linear_flops(s, batch) + decode_attention_flops(s, batch, attend_len)
+
+
+def kv_bytes_per_token(s, elem_bytes=2):
+    return 2 * s.n_kv * s.head_dim * elem_bytes
+
+
+def decode_attention_bytes(s, batch, attend_len, elem_bytes=2):
+    """K and V of every visible slot read once (the query/output are negligible)."""
+    return batch * attend_len * kv_bytes_per_token(s, elem_bytes)
+
+
+def decode_weight_bytes(s, elem_bytes=2):
+    return block_params(s) * elem_bytes
+
+
+def gemm_flops(m, n, k):
+    return 2 * m * n * k

@@ -1,0 +1,44 @@
+"""The work model against the counts printed on "LLaMA-3 8B 现代 LLM 架构、计算规模与能耗"
+(§六 parameter tables, §七 KV-cache sizes, §八 prefill FLOPs, §九 decode FLOPs)."""
+
+import pytest
+
+from llama_decoder_block_amd import workmodel as wm
+
+L3_8B = wm.Shape(d_model=4096, n_q=32, n_kv=8, head_dim=128, d_ff=14336)
+
+
+def test_parameter_counts_llama3_8b():
+    assert wm.attention_params(L3_8B) == 41_943_040
+    assert wm.mlp_params(L3_8B) == 176_160_768
+    assert wm.block_params(L3_8B) == 218_112_000
+    assert wm.linear_params(L3_8B) == 218_103_808
+    mha = wm.Shape(4096, 32, 32, 128, 14336)
+    assert wm.attention_params(mha) == 67_108_864
+
+
+@pytest.mark.parametrize("seq,lin,att", [(128, 5.58e10, 2.68e8), (1024, 4.47e11, 1.72e10),
+                                         (8192, 3.57e12, 1.10e12)])
+def test_prefill_flops_table(seq, lin, att):
+    assert wm.prefill_linear_flops(L3_8B, seq) == pytest.approx(lin, rel=5e-3)
+    assert wm.dense_attention_flops(L3_8B, 1, seq) == pytest.approx(att, rel=5e-3)
+
+
+def test_prefill_total_and_causal_count():
+    total_dense = wm.prefill_linear_flops(L3_8B, 8192) + wm.dense_attention_flops(L3_8B, 1, 8192)
+    assert total_dense == pytest.approx(4.67e12, rel=5e-3)
+    # causal count keeps only the visible half (plus the diagonal)
+    assert wm.prefill_attention_flops(L3_8B, 1, 8192) == 4 * 128 * 32 * 8192 * 8193 // 2
+
+
+def test_decode_flops():
+    assert wm.prefill_linear_flops(L3_8B, 1) == pytest.approx(4.36e8, rel=5e-3)
+    assert wm.decode_attention_flops(L3_8B, 1, 8193) == pytest.approx(2 * 6.71e7, rel=5e-3)
+    assert wm.decode_flops(L3_8B, 1, 8193) == pytest.approx(5.70e8, rel=5e-3)
+
+
+def test_kv_cache_bytes():
+    assert wm.kv_bytes_per_token(L3_8B) == 4096
+    assert 32 * wm.kv_bytes_per_token(wm.Shape(4096, 32, 32, 128, 14336)) == 524_288
+    # 8192-token context over 32 layers is 1 GiB
+    assert 32 * 8192 * wm.kv_bytes_per_token(L3_8B) == 1 << 30
