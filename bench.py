@@ -1,0 +1,228 @@
+"""Throughput of the Llama decoder-block forward on one MI355X.
+
+Default run (python bench.py): W warm-up steps, then K timed steps of the
+Llama-3-8B-shaped prefill block forward (B=1, T=8192, d=4096, 32/8 heads,
+hd=128, d_ff=14336, theta=5e5, bf16 operands, fp32 residual stream), followed
+by the same protocol for the Llama-3-8B-shaped decode step (64 sequences, one
+token each at position 4096 against a 4097-slot bf16 KV cache).  Inputs are
+seeded synthetic tensors already resident in device memory.  Prints one JSON
+line (rank 0).
+
+value      = prefill block-forward TFLOP/s (algorithmic FLOPs: linear layers
+             plus causal attention pairs) over the K timed steps
+roofline   = the dominant kernel (fused gate/up GEMM + SiLU product):
+             algorithmic FLOPs per launch / its average launch time, measured
+             with HIP events recorded on the kernel's stream inside the timed
+             region
+decode     = the decode step: tokens/s, microseconds per step, and the split-K
+             attention kernel's achieved GB/s against the HBM peak
+cpu_baseline = the CPU oracle (numpy fp64) on a bounded sample of the same
+             prefill workload: the first T_s tokens of the sequence
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from llama_decoder_block_amd import binding, synth  # noqa: E402
+from llama_decoder_block_amd import workmodel as wm  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16
+HBM_PEAK_GBS = 8000.0
+
+PREFILL = "llama3_8b_gqa_prefill"
+DECODE = "llama3_8b_gqa_decode"
+DOMINANT = "gemm_mfma_gate_up_silu"
+DECODE_ATTN = "attn_decode_splitk"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def shape_of(wl):
+    return wm.Shape(wl.d_model, wl.n_q, wl.n_kv, wl.head_dim, wl.d_ff)
+
+
+def prepare(wl, dev):
+    inp = synth.make_block_inputs(wl)
+    w = {k: v.to(dev) for k, v in inp.weights.items()}
+    x = inp.x.to(dev)
+    pos = inp.positions.to(dev)
+    kc = inp.k_cache.to(dev) if inp.k_cache is not None else None
+    vc = inp.v_cache.to(dev) if inp.v_cache is not None else None
+    kv_cap = kc.shape[1] if kc is not None else 0
+    hd = wl.head_dim
+    need = binding.block_workspace_bytes(wl.batch, wl.seq, wl.d_model, wl.n_q, wl.n_kv, hd, wl.d_ff, kv_cap,
+                                         binding.BF16, binding.F32)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+
+    def step():
+        binding.block_forward(x, w, pos, wl.n_q, wl.n_kv, wl.theta, wl.eps, k_cache=kc, v_cache=vc, y=y,
+                              workspace=ws)
+    return step, inp
+
+
+def time_steps(step, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.profile_reset()
+    binding.profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    binding.profile_enable(False)
+    kernels = binding.profile_collect()
+    ms = e0.elapsed_time(e1) / steps
+    return ms, wall, kernels
+
+
+def cpu_baseline(tokens):
+    """The oracle (plain numpy fp64) on the first `tokens` tokens of the prefill
+    workload: a causal prefix is itself a complete prefill of that length."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    wl = synth.workload(PREFILL, seq=tokens)
+    inp = synth.make_block_inputs(wl)
+    f = inp.as_f64()
+    t0 = time.perf_counter()
+    oracle.block_forward(f["x"], f["w"], f["positions"], wl.theta, wl.eps, wl.n_q, wl.n_kv)
+    dt = time.perf_counter() - t0
+    flops = wm.prefill_flops(shape_of(wl), wl.batch, wl.seq)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"numpy fp64 block forward of the first {tokens} tokens of the T=8192 Llama-3-8B "
+                      f"prefill (same seeded inputs), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md on sharding); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    binding.lib()
+
+    # ---------------- prefill -----------------
+    wl = synth.workload(PREFILL)
+    log(f"[bench] preparing {PREFILL}")
+    step, _ = prepare(wl, dev)
+    log(f"[bench] prefill: warmup {args.warmup}, timing {args.steps} steps")
+    ms, wall, kernels = time_steps(step, args.steps, args.warmup)
+    sh = shape_of(wl)
+    flops = wm.prefill_flops(sh, wl.batch, wl.seq)
+    tflops = flops / (ms * 1e-3) / 1e12
+    tok_s = wl.batch * wl.seq / (ms * 1e-3)
+    n_dom, ms_dom = kernels.get(DOMINANT, (0, 0.0))
+    dom_flops = wm.gemm_flops(wl.batch * wl.seq, 2 * wl.d_ff, wl.d_model)
+    dom_avg_ms = ms_dom / max(n_dom, 1)
+    dom_tflops = dom_flops / (dom_avg_ms * 1e-3) / 1e12 if n_dom else 0.0
+    log(f"[bench] prefill {ms:.3f} ms/step, {tflops:.1f} TFLOP/s, {tok_s/1e6:.3f} M tok/s")
+    for k, (n, t) in sorted(kernels.items(), key=lambda kv: -kv[1][1]):
+        log(f"[bench]   {k:28s} launches={n:4d} avg={t / n * 1e3:9.1f} us  share={t / (ms * args.steps):6.1%}")
+    del step
+    torch.cuda.empty_cache()
+
+    # ---------------- decode -----------------
+    decode = None
+    if not args.no_decode:
+        wd = synth.workload(DECODE)
+        log(f"[bench] preparing {DECODE}")
+        dstep, _ = prepare(wd, dev)
+        dms, _, dk = time_steps(dstep, args.decode_steps, args.warmup)
+        shd = shape_of(wd)
+        attend = wd.decode_pos + 1
+        n_at, ms_at = dk.get(DECODE_ATTN, (0, 0.0))
+        # attention: the split-K kernel plus its combine pass are timed together
+        at_avg = ms_at / max(n_at, 1)
+        at_bytes = wm.decode_attention_bytes(shd, wd.batch, attend)
+        at_gbs = at_bytes / (at_avg * 1e-3) / 1e9 if n_at else 0.0
+        step_bytes = at_bytes + wm.decode_weight_bytes(shd)
+        decode = {
+            "workload": f"{DECODE}: B={wd.batch} x 1 token at position {wd.decode_pos}, KV cache "
+                        f"[{wd.batch},{wd.kv_cap},{wd.n_kv},{wd.head_dim}] bf16",
+            "ms_per_step": round(dms, 4),
+            "tokens_per_s": round(wd.batch / (dms * 1e-3), 1),
+            "step_tflops": round(wm.decode_flops(shd, wd.batch, attend) / (dms * 1e-3) / 1e12, 3),
+            "step_gbs": round(step_bytes / (dms * 1e-3) / 1e9, 1),
+            "step_hbm_frac": round(step_bytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "attention": {"kernel": DECODE_ATTN, "avg_us": round(at_avg * 1e3, 2),
+                          "bytes": at_bytes, "achieved": round(at_gbs, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(at_gbs / HBM_PEAK_GBS, 4)},
+            "kernels_us": {k: round(t / n * 1e3, 2) for k, (n, t) in dk.items()},
+        }
+        log(f"[bench] decode {dms * 1e3:.1f} us/step, attention {at_avg * 1e3:.1f} us = {at_gbs:.0f} GB/s")
+        for k, (n, t) in sorted(dk.items(), key=lambda kv: -kv[1][1]):
+            log(f"[bench]   {k:28s} launches={n:4d} avg={t / n * 1e3:9.1f} us")
+        del dstep
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(args.cpu_tokens)
+
+    out = {
+        "metric": "block fwd TFLOP/s + tokens/s (prefill & decode), % of MFMA/HBM roofline",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{PREFILL}: B={wl.batch} T={wl.seq} d={wl.d_model} n_q={wl.n_q} "
+                               f"n_kv={wl.n_kv} hd={wl.head_dim} d_ff={wl.d_ff} theta={wl.theta:g}",
+                   "global_batch": wl.batch, "seq_len": wl.seq, "parallelism": "single-gpu"},
+        "tokens_per_s": round(tok_s, 1),
+        "prefill_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": DOMINANT, "bound": "mfma", "achieved": round(dom_tflops, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": dom_flops, "avg_us": round(dom_avg_ms * 1e3, 2)},
+        "kernels_us": {k: round(t / n * 1e3, 2) for k, (n, t) in kernels.items()},
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

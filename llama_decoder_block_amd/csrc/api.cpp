@@ -1,0 +1,526 @@
+// C ABI of the Llama decoder-block library (declared in include/llama_block.h).
+//
+// Host side only: argument validation (before anything is enqueued),
+// workspace carve-up, RoPE frequency table (fp64), launch sequencing on the
+// caller's stream and the optional per-kernel event timing.  No device
+// memory is allocated and the stream is never synchronized.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/llama_block.h"
+#include "kernels.hpp"
+
+using lb::DType;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return LLAMA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(int t) { return t == LLAMA_F32 || t == LLAMA_BF16; }
+
+size_t align_up(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+struct PendingTiming {
+  std::string name;
+  hipEvent_t start, stop;
+};
+struct TimingTotal {
+  int64_t launches = 0;
+  double ms = 0.0;
+};
+bool g_prof_on = false;
+std::vector<PendingTiming> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+std::map<std::string, TimingTotal> g_totals;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (which enqueues exactly the kernels of one named step) and,
+// when timing is on, brackets it with events on the same stream.
+template <class F>
+hipError_t timed(const char* fallback_name, hipStream_t s, F&& launch) {
+  if (!g_prof_on) {
+    const char* name = nullptr;
+    return launch(&name);
+  }
+  hipEvent_t e0 = take_event(), e1 = take_event();
+  if (e0) (void)hipEventRecord(e0, s);
+  const char* name = nullptr;
+  hipError_t err = launch(&name);
+  if (e1) (void)hipEventRecord(e1, s);
+  if (e0 && e1)
+    g_pending.push_back({name ? name : fallback_name, e0, e1});
+  return err;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(LLAMA_ERR_HIP, "%s: HIP error %d (%s)", what, static_cast<int>(e), hipGetErrorString(e));
+}
+
+lb::RopeTable make_rope(int hd, double theta) {
+  lb::RopeTable t{};
+  for (int k = 0; k < hd / 2 && k < 128; ++k)
+    t.inv_freq[k] = std::pow(theta, -2.0 * k / static_cast<double>(hd));
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// shared validation helpers
+// ---------------------------------------------------------------------------
+int check_heads(int32_t nq, int32_t nkv, int32_t hd) {
+  if (nq <= 0 || nkv <= 0 || hd <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "head counts and head_dim must be positive (n_q=%d n_kv=%d hd=%d)", nq, nkv, hd);
+  if (nq % nkv != 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", nq, nkv);
+  if (hd % 2 != 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "head_dim (%d) must be even", hd);
+  if (hd > 256) return fail(LLAMA_ERR_UNSUPPORTED, "head_dim (%d) > 256 is not supported", hd);
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* llama_last_error(void) { return g_last_error.c_str(); }
+
+const char* llama_status_string(int status) {
+  switch (status) {
+    case LLAMA_OK: return "ok";
+    case LLAMA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LLAMA_ERR_UNSUPPORTED: return "unsupported";
+    case LLAMA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case LLAMA_ERR_HIP: return "hip error";
+    default: return "unknown status";
+  }
+}
+
+int llama_version(void) { return LLAMA_BLOCK_VERSION; }
+
+// ---------------------------------------------------------------------------
+int llama_rmsnorm(const void* x, const void* residual, const void* gamma, void* out,
+                  void* sum_out, int64_t n_rows, int32_t d_model, double eps, int wdtype,
+                  int rdtype, void* stream) {
+  if (!dtype_ok(wdtype) || !dtype_ok(rdtype))
+    return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code (wdtype=%d rdtype=%d)", wdtype, rdtype);
+  if (n_rows < 0 || d_model <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "n_rows must be >= 0 and d_model > 0 (n_rows=%lld d_model=%d)",
+                static_cast<long long>(n_rows), d_model);
+  if (!(eps >= 0.0)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  if (n_rows > 0 && (!x || !gamma || !out))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "x, gamma and out must be non-null");
+  if (out && (out == x || (residual && out == residual)))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "out must not alias x or residual");
+  for (const void* p : std::initializer_list<const void*>{x, residual, gamma, static_cast<const void*>(out), static_cast<const void*>(sum_out)})
+    if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  if (n_rows > 0x7fffffff) return fail(LLAMA_ERR_UNSUPPORTED, "n_rows too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("rmsnorm", s, [&](const char** name) {
+    *name = "rmsnorm";
+    return lb::launch_rmsnorm(x, residual, gamma, out, sum_out, n_rows, d_model,
+                              static_cast<float>(eps), static_cast<DType>(wdtype),
+                              static_cast<DType>(rdtype), s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_rmsnorm");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+int llama_rope(void* q, void* k, const int32_t* positions, int64_t n_tokens, int32_t n_q_heads,
+               int32_t n_kv_heads, int32_t head_dim, double rope_theta, int wdtype,
+               void* stream) {
+  if (!dtype_ok(wdtype)) return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code %d", wdtype);
+  if (n_tokens < 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0");
+  if (head_dim <= 0 || head_dim % 2 != 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "head_dim (%d) must be positive and even", head_dim);
+  if (head_dim > 256) return fail(LLAMA_ERR_UNSUPPORTED, "head_dim (%d) > 256 is not supported", head_dim);
+  if (q && n_q_heads <= 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "n_q_heads must be positive");
+  if (k && n_kv_heads <= 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "n_kv_heads must be positive");
+  if (!(rope_theta > 0.0)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "rope_theta must be > 0");
+  if (n_tokens > 0 && !positions) return fail(LLAMA_ERR_INVALID_ARGUMENT, "positions must be non-null");
+  if (n_tokens > 0 && !q && !k) return fail(LLAMA_ERR_INVALID_ARGUMENT, "q and k are both null");
+  for (const void* p : std::initializer_list<const void*>{static_cast<const void*>(q), static_cast<const void*>(k)})
+    if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const lb::RopeTable tab = make_rope(head_dim, rope_theta);
+  hipError_t e = timed("rope", s, [&](const char** name) {
+    *name = "rope";
+    return lb::launch_rope(q, k, positions, n_tokens, n_q_heads, n_kv_heads, head_dim, tab,
+                           static_cast<DType>(wdtype), s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_rope");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+size_t llama_gqa_attention_workspace_bytes(int32_t batch, int32_t q_len, int32_t kv_len,
+                                           int32_t n_q_heads, int32_t n_kv_heads,
+                                           int32_t head_dim, int wdtype) {
+  if (batch <= 0 || q_len <= 0 || kv_len <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+      !dtype_ok(wdtype))
+    return 0;
+  return lb::attention_workspace_bytes(static_cast<DType>(wdtype), batch, q_len, kv_len, n_q_heads,
+                                       n_kv_heads, head_dim);
+}
+
+int llama_gqa_attention(const void* q, const void* k, const void* v, void* out,
+                        const int32_t* positions, int32_t batch, int32_t q_len, int32_t kv_len,
+                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int wdtype,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(wdtype)) return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code %d", wdtype);
+  if (batch < 0 || q_len < 0 || kv_len <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "batch, q_len must be >= 0 and kv_len > 0");
+  int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+  if (st != LLAMA_OK) return st;
+  if (!positions && kv_len < q_len)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "without positions kv_len (%d) must be >= q_len (%d)", kv_len, q_len);
+  if (batch > 0 && q_len > 0 && (!q || !k || !v || !out))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "q, k, v and out must be non-null");
+  if (out && (out == q || out == k || out == v))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "out must not alias q, k or v");
+  for (const void* p : std::initializer_list<const void*>{q, k, v, static_cast<const void*>(out), workspace})
+    if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  if (batch == 0 || q_len == 0) return ok();
+  const size_t need = llama_gqa_attention_workspace_bytes(batch, q_len, kv_len, n_q_heads, n_kv_heads,
+                                                          head_dim, wdtype);
+  if (ws_bytes < need || (need > 0 && !workspace))
+    return fail(LLAMA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  lb::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.positions = positions;
+  a.B = batch; a.Tq = q_len; a.S = kv_len; a.nq = n_q_heads; a.nkv = n_kv_heads; a.hd = head_dim;
+  a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(head_dim)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("attention", s, [&](const char** name) {
+    return lb::launch_attention(static_cast<DType>(wdtype), a, workspace, ws_bytes, s, name);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_gqa_attention");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+
+struct FfnPlan {
+  size_t mact, gemm_gu, gemm_down, total;
+};
+
+FfnPlan ffn_plan(int64_t n, int32_t d, int32_t dff, DType wdt) {
+  FfnPlan p{};
+  p.mact = align_up(static_cast<size_t>(n) * dff * lb::dtype_bytes(wdt));
+  p.gemm_gu = align_up(lb::gemm_workspace_bytes(wdt, static_cast<int>(n), dff, d, true));
+  p.gemm_down = align_up(lb::gemm_workspace_bytes(wdt, static_cast<int>(n), d, dff, false));
+  p.total = p.mact + std::max(p.gemm_gu, p.gemm_down);
+  return p;
+}
+
+// gate/up (+ SiLU product into mact) then down (+ residual) into out
+hipError_t run_ffn(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                   const void* residual, void* out, int n, int d, int dff, DType wdt, DType rdt,
+                   void* mact, void* gws, size_t gws_bytes, hipStream_t s) {
+  lb::WSeg gu{};
+  gu.ptr[0] = w_gate; gu.ptr[1] = w_up; gu.start[0] = 0; gu.start[1] = dff; gu.start[2] = 2 * dff; gu.nseg = 2;
+  lb::GemmEpi e1{};
+  e1.kind = lb::EpiKind::Silu; e1.out_dt = wdt; e1.out = mact; e1.ldo = dff;
+  hipError_t e = timed("gemm_gate_up", s, [&](const char** name) {
+    return lb::launch_gemm(wdt, x, n, d, gu, dff, true, e1, gws, gws_bytes, s, name);
+  });
+  if (e != hipSuccess) return e;
+  lb::WSeg dn{};
+  dn.ptr[0] = w_down; dn.start[0] = 0; dn.start[1] = d; dn.nseg = 1;
+  lb::GemmEpi e2{};
+  if (residual) {
+    e2.kind = lb::EpiKind::Resid; e2.out_dt = rdt; e2.out = out; e2.resid = residual; e2.ldo = d;
+  } else {
+    e2.kind = lb::EpiKind::Store; e2.out_dt = rdt; e2.out = out; e2.ldo = d;
+  }
+  return timed("gemm_down", s, [&](const char** name) {
+    return lb::launch_gemm(wdt, mact, n, dff, dn, d, false, e2, gws, gws_bytes, s, name);
+  });
+}
+
+}  // namespace
+
+size_t llama_swiglu_ffn_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t d_ff, int wdtype,
+                                        int rdtype) {
+  if (n_tokens <= 0 || d_model <= 0 || d_ff <= 0 || !dtype_ok(wdtype) || !dtype_ok(rdtype)) return 0;
+  return ffn_plan(n_tokens, d_model, d_ff, static_cast<DType>(wdtype)).total;
+}
+
+int llama_swiglu_ffn(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                     const void* residual, void* out, int64_t n_tokens, int32_t d_model,
+                     int32_t d_ff, int wdtype, int rdtype, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  if (!dtype_ok(wdtype) || !dtype_ok(rdtype))
+    return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code (wdtype=%d rdtype=%d)", wdtype, rdtype);
+  if (n_tokens < 0 || d_model <= 0 || d_ff <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0, d_model and d_ff > 0");
+  if (n_tokens > 0x7fffffff) return fail(LLAMA_ERR_UNSUPPORTED, "n_tokens too large");
+  if (n_tokens > 0 && (!x || !w_gate || !w_up || !w_down || !out))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "x, weights and out must be non-null");
+  if (out && out == x) return fail(LLAMA_ERR_INVALID_ARGUMENT, "out must not alias x");
+  for (const void* p : std::initializer_list<const void*>{x, w_gate, w_up, w_down, residual, static_cast<const void*>(out), workspace})
+    if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  if (n_tokens == 0) return ok();
+  const DType wdt = static_cast<DType>(wdtype), rdt = static_cast<DType>(rdtype);
+  const FfnPlan p = ffn_plan(n_tokens, d_model, d_ff, wdt);
+  if (ws_bytes < p.total || !workspace)
+    return fail(LLAMA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total, ws_bytes);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipError_t e = run_ffn(x, w_gate, w_up, w_down, residual, out, static_cast<int>(n_tokens), d_model, d_ff,
+                         wdt, rdt, ws, ws + p.mact, ws_bytes - p.mact, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "llama_swiglu_ffn");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+
+struct BlockPlan {
+  size_t a, q, k, v, o, h, mact, attn, gemm, total;
+};
+
+BlockPlan block_plan(int B, int T, int d, int nq, int nkv, int hd, int dff, int kv_cap, DType wdt,
+                     DType rdt) {
+  const size_t M = static_cast<size_t>(B) * T;
+  const size_t wb = lb::dtype_bytes(wdt), rb = lb::dtype_bytes(rdt);
+  BlockPlan p{};
+  p.a = align_up(M * d * wb);  // also holds f (the FFN pre-norm output)
+  p.q = align_up(M * nq * hd * wb);
+  p.k = kv_cap > 0 ? 0 : align_up(M * nkv * hd * wb);
+  p.v = p.k;
+  p.o = align_up(M * nq * hd * wb);
+  p.h = align_up(M * d * rb);
+  p.mact = align_up(M * dff * wb);
+  const int S = kv_cap > 0 ? kv_cap : T;
+  p.attn = align_up(lb::attention_workspace_bytes(wdt, B, T, S, nq, nkv, hd));
+  size_t g = lb::gemm_workspace_bytes(wdt, static_cast<int>(M), (nq + 2 * nkv) * hd, d, false);
+  g = std::max(g, lb::gemm_workspace_bytes(wdt, static_cast<int>(M), d, nq * hd, false));
+  g = std::max(g, lb::gemm_workspace_bytes(wdt, static_cast<int>(M), dff, d, true));
+  g = std::max(g, lb::gemm_workspace_bytes(wdt, static_cast<int>(M), d, dff, false));
+  p.gemm = align_up(g);
+  p.total = p.a + p.q + p.k + p.v + p.o + p.h + p.mact + p.attn + p.gemm;
+  return p;
+}
+
+}  // namespace
+
+size_t llama_block_forward_workspace_bytes(int32_t batch, int32_t seq_len, int32_t d_model,
+                                           int32_t n_q_heads, int32_t n_kv_heads,
+                                           int32_t head_dim, int32_t d_ff, int32_t kv_cap,
+                                           int wdtype, int rdtype) {
+  if (batch <= 0 || seq_len <= 0 || d_model <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+      d_ff <= 0 || kv_cap < 0 || !dtype_ok(wdtype) || !dtype_ok(rdtype))
+    return 0;
+  return block_plan(batch, seq_len, d_model, n_q_heads, n_kv_heads, head_dim, d_ff, kv_cap,
+                    static_cast<DType>(wdtype), static_cast<DType>(rdtype))
+      .total;
+}
+
+int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
+                        const int32_t* positions, void* k_cache, void* v_cache, int32_t kv_cap,
+                        int32_t batch, int32_t seq_len, int32_t d_model, int32_t n_q_heads,
+                        int32_t n_kv_heads, int32_t head_dim, int32_t d_ff, double rope_theta,
+                        double eps, int wdtype, int rdtype, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  if (!dtype_ok(wdtype) || !dtype_ok(rdtype))
+    return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code (wdtype=%d rdtype=%d)", wdtype, rdtype);
+  if (batch < 0 || seq_len < 0 || d_model <= 0 || d_ff <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "batch, seq_len must be >= 0; d_model, d_ff > 0");
+  int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+  if (st != LLAMA_OK) return st;
+  if (!(rope_theta > 0.0)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "rope_theta must be > 0");
+  if (!(eps >= 0.0)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  if (kv_cap < 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "kv_cap must be >= 0");
+  const bool has_cache = kv_cap > 0;
+  if (has_cache != (k_cache != nullptr) || has_cache != (v_cache != nullptr))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "k_cache and v_cache must both be given exactly when kv_cap > 0");
+  if (static_cast<int64_t>(batch) * seq_len > 0x7fffffff)
+    return fail(LLAMA_ERR_UNSUPPORTED, "batch*seq_len too large");
+  if (batch == 0 || seq_len == 0) return ok();
+  if (!x || !y || !w || !positions)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "x, y, weights and positions must be non-null");
+  if (!w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->ffn_norm || !w->w_gate || !w->w_up ||
+      !w->w_down)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "every weight pointer must be non-null");
+  if (y == x) return fail(LLAMA_ERR_INVALID_ARGUMENT, "y must not alias x");
+  for (const void* p : std::initializer_list<const void*>{x, static_cast<const void*>(y), w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->ffn_norm,
+                        w->w_gate, w->w_up, w->w_down, static_cast<const void*>(k_cache),
+                        static_cast<const void*>(v_cache), workspace})
+    if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+
+  const DType wdt = static_cast<DType>(wdtype), rdt = static_cast<DType>(rdtype);
+  const int B = batch, T = seq_len, d = d_model, nq = n_q_heads, nkv = n_kv_heads, hd = head_dim;
+  const int M = B * T;
+  const BlockPlan p = block_plan(B, T, d, nq, nkv, hd, d_ff, kv_cap, wdt, rdt);
+  if (ws_bytes < p.total || !workspace)
+    return fail(LLAMA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total, ws_bytes);
+
+  uint8_t* cur = static_cast<uint8_t*>(workspace);
+  auto carve = [&](size_t n) { uint8_t* r = cur; cur += n; return r; };
+  void* a_buf = carve(p.a);
+  void* q_buf = carve(p.q);
+  void* k_buf = has_cache ? k_cache : carve(p.k);
+  void* v_buf = has_cache ? v_cache : carve(p.v);
+  void* o_buf = carve(p.o);
+  void* h_buf = carve(p.h);
+  void* mact = carve(p.mact);
+  void* attn_ws = carve(p.attn);
+  void* gemm_ws = carve(p.gemm);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const lb::RopeTable rope = make_rope(hd, rope_theta);
+  const float feps = static_cast<float>(eps);
+  hipError_t e;
+
+  // a1: attention pre-norm
+  e = timed("rmsnorm", s, [&](const char** name) {
+    *name = "rmsnorm";
+    return lb::launch_rmsnorm(x, nullptr, w->attn_norm, a_buf, nullptr, M, d, feps, wdt, rdt, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_block_forward: attention norm");
+
+  // a2-a4: fused Q/K/V projection with RoPE and (cache) stores
+  {
+    lb::WSeg wqkv{};
+    wqkv.ptr[0] = w->wq; wqkv.ptr[1] = w->wk; wqkv.ptr[2] = w->wv;
+    wqkv.start[0] = 0; wqkv.start[1] = nq * hd; wqkv.start[2] = (nq + nkv) * hd;
+    wqkv.start[3] = (nq + 2 * nkv) * hd; wqkv.nseg = 3;
+    lb::GemmEpi ep{};
+    ep.kind = lb::EpiKind::Qkv; ep.out_dt = wdt;
+    ep.q = q_buf; ep.k = k_buf; ep.v = v_buf; ep.positions = positions;
+    ep.nq_hd = nq * hd; ep.nkv_hd = nkv * hd; ep.hd = hd; ep.seq_len = T; ep.kv_cap = kv_cap;
+    ep.rope = &rope;
+    e = timed("gemm_qkv_rope", s, [&](const char** name) {
+      return lb::launch_gemm(wdt, a_buf, M, d, wqkv, (nq + 2 * nkv) * hd, false, ep, gemm_ws, p.gemm, s, name);
+    });
+    if (e != hipSuccess) return hip_fail(e, "llama_block_forward: qkv projection");
+  }
+
+  // a5/a6: attention
+  {
+    lb::AttnArgs aa{};
+    aa.q = q_buf; aa.k = k_buf; aa.v = v_buf; aa.out = o_buf;
+    aa.positions = has_cache ? positions : nullptr;
+    aa.B = B; aa.Tq = T; aa.S = has_cache ? kv_cap : T; aa.nq = nq; aa.nkv = nkv; aa.hd = hd;
+    aa.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(hd)));
+    e = timed("attention", s, [&](const char** name) {
+      return lb::launch_attention(wdt, aa, attn_ws, p.attn, s, name);
+    });
+    if (e != hipSuccess) return hip_fail(e, "llama_block_forward: attention");
+  }
+
+  // a7: O projection + residual into h
+  {
+    lb::WSeg wo{};
+    wo.ptr[0] = w->wo; wo.start[0] = 0; wo.start[1] = d; wo.nseg = 1;
+    lb::GemmEpi ep{};
+    ep.kind = lb::EpiKind::Resid; ep.out_dt = rdt; ep.out = h_buf; ep.resid = x; ep.ldo = d;
+    e = timed("gemm_o_resid", s, [&](const char** name) {
+      return lb::launch_gemm(wdt, o_buf, M, nq * hd, wo, d, false, ep, gemm_ws, p.gemm, s, name);
+    });
+    if (e != hipSuccess) return hip_fail(e, "llama_block_forward: o projection");
+  }
+
+  // a8: FFN pre-norm (f reuses the a buffer)
+  e = timed("rmsnorm", s, [&](const char** name) {
+    *name = "rmsnorm";
+    return lb::launch_rmsnorm(h_buf, nullptr, w->ffn_norm, a_buf, nullptr, M, d, feps, wdt, rdt, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_block_forward: ffn norm");
+
+  // a9/a10: SwiGLU FFN + residual into y
+  e = run_ffn(a_buf, w->w_gate, w->w_up, w->w_down, h_buf, y, M, d, d_ff, wdt, rdt, mact, gemm_ws, p.gemm, s);
+  if (e != hipSuccess) return hip_fail(e, "llama_block_forward: ffn");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+int llama_profile_enable(int on) {
+  g_prof_on = on != 0;
+  return ok();
+}
+
+int llama_profile_reset(void) {
+  for (auto& pt : g_pending) {
+    g_event_pool.push_back(pt.start);
+    g_event_pool.push_back(pt.stop);
+  }
+  g_pending.clear();
+  g_totals.clear();
+  return ok();
+}
+
+int llama_profile_collect(void) {
+  for (auto& pt : g_pending) {
+    hipError_t e = hipEventSynchronize(pt.stop);
+    if (e != hipSuccess) return hip_fail(e, "llama_profile_collect");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, pt.start, pt.stop);
+    if (e != hipSuccess) return hip_fail(e, "llama_profile_collect");
+    TimingTotal& t = g_totals[pt.name];
+    t.launches += 1;
+    t.ms += ms;
+    g_event_pool.push_back(pt.start);
+    g_event_pool.push_back(pt.stop);
+  }
+  g_pending.clear();
+  return ok();
+}
+
+int llama_profile_query(const char* kernel_name, int64_t* launches, double* total_ms) {
+  if (!kernel_name) return fail(LLAMA_ERR_INVALID_ARGUMENT, "kernel_name is null");
+  auto it = g_totals.find(kernel_name);
+  if (it == g_totals.end()) return fail(LLAMA_ERR_INVALID_ARGUMENT, "no timing recorded for '%s'", kernel_name);
+  if (launches) *launches = it->second.launches;
+  if (total_ms) *total_ms = it->second.ms;
+  return ok();
+}
+
+int llama_profile_names(char* buf, size_t cap) {
+  std::string all;
+  for (auto& kv : g_totals) {
+    all += kv.first;
+    all += '\n';
+  }
+  if (!buf || cap == 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "buffer is null or empty");
+  std::strncpy(buf, all.c_str(), cap - 1);
+  buf[cap - 1] = '\0';
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,595 @@
+// Causal grouped-query attention: o = softmax(q.k / sqrt(hd) over visible
+// slots) . V, query head h reading KV head floor(h / (n_q/n_kv))
+// ("Llama Architecture: RMSNorm, SwiGLU, RoPE, GQA, and PyTorch Implementation"
+// §4 GQA equation; "LLaMA-3 8B 现代 LLM 架构、计算规模与能耗" §4.4-4.7, which also
+// notes that the shared K/V need not be copied per query head and that a
+// tiled on-chip softmax gives the same result as the full matrix).
+//
+// attn_flash_kernel (bf16, hd = 128, prefill): one workgroup per (sequence,
+//   KV group, tile of 128 query rows) where the rows are the R = n_q/n_kv
+//   heads of the group times 128/R tokens.  Each K/V tile of 64 slots is
+//   staged once in LDS and used by all R heads.  Four wavefronts own 32 query
+//   rows each.  Scores are computed transposed (S^T = K Q^T on
+//   v_mfma_f32_32x32x16_bf16) so that every lane holds 32 scores of ONE query
+//   row: the online-softmax max/sum need only one cross-lane exchange, and the
+//   probabilities already sit in the register layout of the B operand of
+//   O^T = V^T P^T.  V is written to LDS transposed for that product.
+//   Accumulators, running max and sum are fp32; P is rounded to bf16 for the
+//   MFMA.  Only tiles at or below each workgroup's last visible slot are read.
+// attn_decode_kernel (one query token per sequence): split-K over the key
+//   slots.  One workgroup per (sequence, KV group, chunk of 256 slots) streams
+//   its chunk of K and V once (16-byte loads, all issued up front) for the R
+//   query heads of the group and writes a partial (max, sum, output);
+//   attn_decode_combine_kernel merges the chunks.
+// attn_valu_kernel: generic fp32-accumulating kernel (one wavefront per query
+//   row, online softmax over 64-slot chunks) for fp32 and other shapes.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lb {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ===========================================================================
+// generic VALU kernel
+// ===========================================================================
+template <typename T>
+__global__ void __launch_bounds__(256)
+attn_valu_kernel(AttnArgs a) {
+  __shared__ float qs[4][256];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t rid = static_cast<int64_t>(blockIdx.x) * 4 + w;  // (b, t, h), h fastest
+  const int64_t nrows = static_cast<int64_t>(a.B) * a.Tq * a.nq;
+  const bool active = rid < nrows;
+  const int h = active ? static_cast<int>(rid % a.nq) : 0;
+  const int64_t bt = active ? rid / a.nq : 0;
+  const int b = static_cast<int>(bt / a.Tq), t = static_cast<int>(bt % a.Tq);
+  const T* q = static_cast<const T*>(a.q) + rid * a.hd;
+  if (active)
+    for (int d = lane; d < a.hd; d += 64) qs[w][d] = ld(q + d);
+  __syncthreads();
+  if (!active) return;
+  const int g = h / (a.nq / a.nkv);
+  const int vis = a.positions ? a.positions[bt] : t;
+  const T* kb = static_cast<const T*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * a.hd;
+  const T* vb = static_cast<const T*>(a.v) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * a.hd;
+  const int64_t kstride = static_cast<int64_t>(a.nkv) * a.hd;
+  const float c = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 <= vis; j0 += 64) {
+    const int j = j0 + lane;
+    float s = -INFINITY;
+    if (j <= vis) {
+      const T* kr = kb + j * kstride;
+      float acc = 0.f;
+      for (int d = 0; d < a.hd; ++d) acc += qs[w][d] * ld(kr + d);
+      s = acc * c;
+    }
+    const float mx = wave_max(s);
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    const float p = j <= vis ? exp2f(s - mn) : 0.f;
+    l = l * alpha + wave_sum(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] *= alpha;
+    const int cnt = min(64, vis - j0 + 1);
+    for (int jj = 0; jj < cnt; ++jj) {
+      const float pj = __shfl(p, jj, 64);
+      const T* vr = vb + (j0 + jj) * kstride;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = lane + 64 * i;
+        if (d < a.hd) o[i] += pj * ld(vr + d);
+      }
+    }
+    m = mn;
+  }
+  T* out = static_cast<T*>(a.out) + rid * a.hd;
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d = lane + 64 * i;
+    if (d < a.hd) st(out + d, o[i] * inv);
+  }
+}
+
+// ===========================================================================
+// flash prefill kernel (bf16, hd = 128)
+// ===========================================================================
+constexpr int kFHd = 128;
+constexpr int kFRows = 128;              // query rows per workgroup
+constexpr int kFKeys = 64;               // key slots per tile
+constexpr int kKStride = kFHd * 2 + 16;  // bytes per K row in LDS (padded)
+constexpr int kVStride = kFKeys * 2 + 8; // bytes per V^T row in LDS (padded)
+constexpr int kKBytes = kFKeys * kKStride;
+constexpr int kVBytes = kFHd * kVStride;
+constexpr int kFBufBytes = kKBytes + kVBytes;
+
+template <int R>
+__global__ void __launch_bounds__(256, 2)
+attn_flash_kernel(AttnArgs a, int n_qtiles) {
+  constexpr int TQ = kFRows / R;  // tokens per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kFBufBytes];
+  __shared__ int vis_s[kFRows];
+
+  // heavy tiles (late query tokens) first
+  const int qt = n_qtiles - 1 - static_cast<int>(blockIdx.x % n_qtiles);
+  const int bg = blockIdx.x / n_qtiles;
+  const int g = bg % a.nkv, b = bg / a.nkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t0 = qt * TQ;
+
+  if (tid < kFRows) {
+    const int t = t0 + tid % TQ;
+    int vis = -1;
+    if (t < a.Tq) vis = a.positions ? a.positions[static_cast<int64_t>(b) * a.Tq + t] : t;
+    vis_s[tid] = vis;
+  }
+  __syncthreads();
+  int maxvis = -1;
+  for (int i = 0; i < kFRows; ++i) maxvis = max(maxvis, vis_s[i]);
+  const int my_row = w * 32 + (lane & 31);
+  const int my_vis = vis_s[my_row];
+  int wave_min = 0x7fffffff;
+  for (int i = 0; i < 32; ++i) {
+    const int v = vis_s[w * 32 + i];
+    wave_min = min(wave_min, v < 0 ? 0x7fffffff : v);
+  }
+  const int nkt = maxvis < 0 ? 0 : maxvis / kFKeys + 1;
+
+  const int my_hi = my_row / TQ, my_t = t0 + my_row % TQ;
+  const int my_h = g * R + my_hi;
+  const int half = lane >> 5;
+
+  // Q fragments: B operand, column = query row, k = hd
+  bf16x8 qf[8];
+  {
+    const int tq = min(my_t, a.Tq - 1);
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) +
+                       ((static_cast<int64_t>(b) * a.Tq + tq) * a.nq + my_h) * kFHd;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + half * 8);
+  }
+
+  const int64_t kvrow = static_cast<int64_t>(a.nkv) * kFHd;  // elements between slots
+  const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * kFHd;
+  const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * kFHd;
+
+  // global -> register staging: K: 4 rows x 16 B per thread; V: 4 slots x 8 hd
+  const int k_chunk = tid & 15, k_row = tid >> 4;     // rows k_row + 16 i
+  const int v_kg = tid & 15, v_hc = tid >> 4;         // slots 4*v_kg..+3, hd 8*v_hc..+7
+  u32x4 kreg[4], vreg[4];
+  auto gload = [&](int kt) {
+    const int base = kt * kFKeys;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = min(base + k_row + 16 * i, a.S - 1);
+      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + j * kvrow + k_chunk * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = min(base + 4 * v_kg + i, a.S - 1);
+      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + j * kvrow + v_hc * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* kb = smem + buf * kFBufBytes;
+    uint8_t* vb = kb + kKBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(kb + (k_row + 16 * i) * kKStride + k_chunk * 16) = kreg[i];
+    // transpose 4 slots x 8 hd into 8 rows (hd) of 4 slots
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int word = e >> 1;
+      const bool hi = e & 1;
+      uint32_t s0 = hi ? (vreg[0][word] >> 16) : (vreg[0][word] & 0xffffu);
+      uint32_t s1 = hi ? (vreg[1][word] >> 16) : (vreg[1][word] & 0xffffu);
+      uint32_t s2 = hi ? (vreg[2][word] >> 16) : (vreg[2][word] & 0xffffu);
+      uint32_t s3 = hi ? (vreg[3][word] >> 16) : (vreg[3][word] & 0xffffu);
+      u32x2 pk = {s0 | (s1 << 16), s2 | (s3 << 16)};
+      *reinterpret_cast<u32x2*>(vb + (v_hc * 8 + e) * kVStride + v_kg * 8) = pk;
+    }
+  };
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale * kLog2e;
+
+  if (nkt > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) gload(kt + 1);
+    const uint8_t* kb = smem + buf * kFBufBytes;
+    const uint8_t* vb = kb + kKBytes;
+
+    // S^T = K Q^T for two 32-slot halves
+    f32x16 sacc[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            kb + (h2 * 32 + (lane & 31)) * kKStride + kk * 32 + half * 16);
+        sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[h2], 0, 0, 0);
+      }
+    }
+    // scale, mask, running max
+    const bool need_mask = kt * kFKeys + kFKeys - 1 > wave_min;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float s = sacc[h2][e] * c;
+        if (need_mask) {
+          const int j = kt * kFKeys + h2 * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          if (j > my_vis) s = -INFINITY;
+        }
+        sacc[h2][e] = s;
+        tmax = fmaxf(tmax, s);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 pk;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float p0 = fast_exp2(sacc[h2][hh * 8 + 2 * e2] - m_use);
+          const float p1 = fast_exp2(sacc[h2][hh * 8 + 2 * e2 + 1] - m_use);
+          psum += p0 + p1;
+          pk[e2] = pack_bf16x2(p0, p1);
+        }
+        pf[h2][hh] = __builtin_bit_cast(bf16x8, pk);
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int s0 = h2 * 32 + hh * 16 + half * 4;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint8_t* vr = vb + (d * 32 + (lane & 31)) * kVStride;
+          u32x2 lo = *reinterpret_cast<const u32x2*>(vr + s0 * 2);
+          u32x2 hi = *reinterpret_cast<const u32x2*>(vr + (s0 + 8) * 2);
+          u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                            pf[h2][hh], oacc[d], 0, 0, 0);
+        }
+      }
+    if (kt + 1 < nkt) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // normalise and store: O^T register e of subtile d is hd = d*32 + (e/4)*8 + half*4 + e%4
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (my_t < a.Tq && my_vis >= 0) {
+    const float inv = 1.f / l_tot;
+    bf16_t* op = static_cast<bf16_t*>(a.out) + ((static_cast<int64_t>(b) * a.Tq + my_t) * a.nq + my_h) * kFHd;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = oacc[d][j * 4 + i] * inv;
+        Vec4<bf16_t>::store(op + d * 32 + j * 8 + half * 4, v);
+      }
+  }
+}
+
+// ===========================================================================
+// split-K decode kernel + combine
+// ===========================================================================
+constexpr int kDChunk = 256;  // key slots per workgroup
+
+template <typename T> struct VecN;            // 16-byte vector of T
+template <> struct VecN<bf16_t> { static constexpr int N = 8; };
+template <> struct VecN<float> { static constexpr int N = 4; };
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const u32x4& r, float* out) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(r[i] << 16);
+      out[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(r[i]);
+  }
+}
+
+// Workgroup: 256 threads.  A K/V row of HD elements is read by L = HD/EPL
+// lanes (16 bytes each); a wavefront covers 64/L slots per load and the
+// workgroup 256/L; each thread issues kDChunk*L/256 loads for K and as many
+// for V.
+template <typename T, int HD, int R>
+__global__ void __launch_bounds__(256)
+attn_decode_kernel(AttnArgs a, int n_chunks, float* __restrict__ part_o,
+                   float* __restrict__ part_ml) {
+  constexpr int EPL = VecN<T>::N;
+  constexpr int L = HD / EPL;               // lanes per slot row
+  constexpr int SLOTS_PER_PASS = 256 / L;   // slots per workgroup load
+  constexpr int PASSES = kDChunk / SLOTS_PER_PASS;
+  static_assert(L >= 1 && L <= 64 && (64 % L) == 0, "bad HD");
+  __shared__ float s_sc[R][kDChunk];
+  __shared__ float s_red[R][256 / L > 0 ? 4 : 1][HD];
+  __shared__ float s_ml[R][2];
+
+  const int chunk = blockIdx.x % n_chunks;
+  const int bg = blockIdx.x / n_chunks;
+  const int g = bg % a.nkv, b = bg / a.nkv;
+  const int vis = a.positions ? a.positions[b] : 0;  // q_len == 1
+  const int j0 = chunk * kDChunk;
+  if (j0 > vis) return;  // nothing visible in this chunk (combine skips it)
+  const int jn = min(kDChunk, vis - j0 + 1);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int sub = tid % L;           // element group within the row
+  const int slot_in_pass = tid / L;  // 0 .. SLOTS_PER_PASS-1
+  const int64_t kvrow = static_cast<int64_t>(a.nkv) * HD;
+  const T* kb = static_cast<const T*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD + sub * EPL;
+  const T* vb = static_cast<const T*>(a.v) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD + sub * EPL;
+
+  // issue every K and V load of this thread
+  u32x4 kr[PASSES], vr[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int jl = p * SLOTS_PER_PASS + slot_in_pass;
+    const int j = j0 + min(jl, jn - 1);
+    kr[p] = *reinterpret_cast<const u32x4*>(kb + j * kvrow);
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int jl = p * SLOTS_PER_PASS + slot_in_pass;
+    const int j = j0 + min(jl, jn - 1);
+    vr[p] = *reinterpret_cast<const u32x4*>(vb + j * kvrow);
+  }
+
+  // this lane's slice of the R query vectors
+  float qv[R][EPL];
+  const T* qb = static_cast<const T*>(a.q) + (static_cast<int64_t>(b) * a.nq + g * R) * HD + sub * EPL;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const u32x4 t = *reinterpret_cast<const u32x4*>(qb + r * HD);
+    unpack16<T>(t, qv[r]);
+  }
+  const float c = a.scale * kLog2e;
+
+  // scores
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    float kv[EPL];
+    unpack16<T>(kr[p], kv);
+    const int jl = p * SLOTS_PER_PASS + slot_in_pass;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc += qv[r][e] * kv[e];
+#pragma unroll
+      for (int off = L / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      if (sub == 0) s_sc[r][jl] = jl < jn ? acc * c : -INFINITY;
+    }
+  }
+  __syncthreads();
+
+  // per-head softmax over the chunk (wave w handles heads w, w+4, ...)
+  for (int r = w; r < R; r += 4) {
+    float mx = -INFINITY;
+    for (int i = lane; i < kDChunk; i += 64) mx = fmaxf(mx, s_sc[r][i]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int i = lane; i < kDChunk; i += 64) {
+      const float p = fast_exp2(s_sc[r][i] - mx);
+      s_sc[r][i] = p;
+      sum += p;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) {
+      s_ml[r][0] = mx;
+      s_ml[r][1] = sum;
+    }
+  }
+  __syncthreads();
+
+  // P V: each thread accumulates its element group over its slots
+  float o[R][EPL];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[r][e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    float vv[EPL];
+    unpack16<T>(vr[p], vv);
+    const int jl = p * SLOTS_PER_PASS + slot_in_pass;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float pr = jl < jn ? s_sc[r][jl] : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[r][e] += pr * vv[e];
+    }
+  }
+  // reduce over the slots handled by different lanes of a wavefront
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float v = o[r][e];
+#pragma unroll
+      for (int off = 32; off >= L; off >>= 1) v += __shfl_xor(v, off, 64);
+      o[r][e] = v;
+    }
+  if (lane < L) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_red[r][w][sub * EPL + e] = o[r][e];
+  }
+  __syncthreads();
+  // reduce over the four wavefronts and write the partial
+  const int64_t pbase = (static_cast<int64_t>(b) * a.nq + g * R) * n_chunks + chunk;
+  for (int i = tid; i < R * HD; i += 256) {
+    const int r = i / HD, d = i % HD;
+    const float v = s_red[r][0][d] + s_red[r][1][d] + s_red[r][2][d] + s_red[r][3][d];
+    part_o[(pbase + static_cast<int64_t>(r) * n_chunks) * HD + d] = v;
+  }
+  if (tid < R) {
+    part_ml[(pbase + static_cast<int64_t>(tid) * n_chunks) * 2 + 0] = s_ml[tid][0];
+    part_ml[(pbase + static_cast<int64_t>(tid) * n_chunks) * 2 + 1] = s_ml[tid][1];
+  }
+}
+
+// one wavefront per (b, h): merge the visible chunks
+template <typename T, int HD>
+__global__ void __launch_bounds__(256)
+attn_decode_combine_kernel(AttnArgs a, int n_chunks, const float* __restrict__ part_o,
+                           const float* __restrict__ part_ml) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + w;
+  if (bh >= static_cast<int64_t>(a.B) * a.nq) return;
+  const int b = static_cast<int>(bh / a.nq);
+  const int vis = a.positions ? a.positions[b] : 0;
+  const int nvalid = min(n_chunks, vis / kDChunk + 1);
+  const float* ml = part_ml + bh * n_chunks * 2;
+  float mx = -INFINITY;
+  for (int ch = 0; ch < nvalid; ++ch) mx = fmaxf(mx, ml[2 * ch]);
+  float lsum = 0.f;
+  float o[HD / 64 > 0 ? HD / 64 : 1] = {};
+  for (int ch = 0; ch < nvalid; ++ch) {
+    const float f = fast_exp2(ml[2 * ch] - mx);
+    lsum += ml[2 * ch + 1] * f;
+    const float* po = part_o + (bh * n_chunks + ch) * HD;
+#pragma unroll
+    for (int i = 0; i < (HD + 63) / 64; ++i) {
+      const int d = lane + 64 * i;
+      if (d < HD) o[i] += po[d] * f;
+    }
+  }
+  const float inv = 1.f / lsum;
+  T* out = static_cast<T*>(a.out) + bh * HD;
+#pragma unroll
+  for (int i = 0; i < (HD + 63) / 64; ++i) {
+    const int d = lane + 64 * i;
+    if (d < HD) st(out + d, o[i] * inv);
+  }
+}
+
+int decode_chunks(int S) { return (S + kDChunk - 1) / kDChunk; }
+
+template <typename T, int HD>
+hipError_t launch_decode_t(const AttnArgs& a, void* ws, hipStream_t s) {
+  const int nch = decode_chunks(a.S);
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + static_cast<int64_t>(a.B) * a.nq * nch * HD;
+  const int R = a.nq / a.nkv;
+  dim3 grid(a.B * a.nkv * nch);
+  switch (R) {
+    case 1: hipLaunchKernelGGL((attn_decode_kernel<T, HD, 1>), grid, dim3(256), 0, s, a, nch, part_o, part_ml); break;
+    case 2: hipLaunchKernelGGL((attn_decode_kernel<T, HD, 2>), grid, dim3(256), 0, s, a, nch, part_o, part_ml); break;
+    case 4: hipLaunchKernelGGL((attn_decode_kernel<T, HD, 4>), grid, dim3(256), 0, s, a, nch, part_o, part_ml); break;
+    case 8: hipLaunchKernelGGL((attn_decode_kernel<T, HD, 8>), grid, dim3(256), 0, s, a, nch, part_o, part_ml); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t waves = static_cast<int64_t>(a.B) * a.nq;
+  hipLaunchKernelGGL((attn_decode_combine_kernel<T, HD>), dim3(static_cast<unsigned>((waves + 3) / 4)),
+                     dim3(256), 0, s, a, nch, part_o, part_ml);
+  return hipGetLastError();
+}
+
+bool decode_supported(DType dt, const AttnArgs& a) {
+  const int R = a.nq / a.nkv;
+  const bool r_ok = R == 1 || R == 2 || R == 4 || R == 8;
+  return a.Tq == 1 && r_ok && (a.hd == 64 || a.hd == 128);
+  (void)dt;
+}
+
+bool flash_supported(DType dt, const AttnArgs& a) {
+  const int R = a.nq / a.nkv;
+  return dt == DType::BF16 && a.Tq > 1 && a.hd == kFHd &&
+         (R == 1 || R == 2 || R == 4 || R == 8);
+}
+
+}  // namespace
+
+size_t attention_workspace_bytes(DType dt, int B, int Tq, int S, int nq, int nkv, int hd) {
+  AttnArgs a{};
+  a.B = B; a.Tq = Tq; a.S = S; a.nq = nq; a.nkv = nkv; a.hd = hd;
+  if (!decode_supported(dt, a)) return 0;
+  const int nch = decode_chunks(S);
+  return static_cast<size_t>(B) * nq * nch * (hd + 2) * sizeof(float);
+}
+
+hipError_t launch_attention(DType dt, const AttnArgs& a, void* ws, size_t ws_bytes,
+                            hipStream_t s, const char** kernel_name) {
+  if (a.B == 0 || a.Tq == 0) return hipSuccess;
+  if (decode_supported(dt, a)) {
+    if (ws_bytes < attention_workspace_bytes(dt, a.B, a.Tq, a.S, a.nq, a.nkv, a.hd))
+      return hipErrorInvalidValue;
+    if (kernel_name) *kernel_name = "attn_decode_splitk";
+    if (dt == DType::BF16)
+      return a.hd == 128 ? launch_decode_t<bf16_t, 128>(a, ws, s) : launch_decode_t<bf16_t, 64>(a, ws, s);
+    return a.hd == 128 ? launch_decode_t<float, 128>(a, ws, s) : launch_decode_t<float, 64>(a, ws, s);
+  }
+  if (flash_supported(dt, a)) {
+    const int R = a.nq / a.nkv;
+    const int TQ = kFRows / R;
+    const int n_qtiles = (a.Tq + TQ - 1) / TQ;
+    dim3 grid(a.B * a.nkv * n_qtiles);
+    if (kernel_name) *kernel_name = "attn_flash_prefill";
+    switch (R) {
+      case 1: hipLaunchKernelGGL((attn_flash_kernel<1>), grid, dim3(256), 0, s, a, n_qtiles); break;
+      case 2: hipLaunchKernelGGL((attn_flash_kernel<2>), grid, dim3(256), 0, s, a, n_qtiles); break;
+      case 4: hipLaunchKernelGGL((attn_flash_kernel<4>), grid, dim3(256), 0, s, a, n_qtiles); break;
+      default: hipLaunchKernelGGL((attn_flash_kernel<8>), grid, dim3(256), 0, s, a, n_qtiles); break;
+    }
+    return hipGetLastError();
+  }
+  if (a.hd > 256) return hipErrorInvalidValue;
+  const int64_t rows = static_cast<int64_t>(a.B) * a.Tq * a.nq;
+  dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  if (kernel_name) *kernel_name = "attn_valu";
+  if (dt == DType::F32)
+    hipLaunchKernelGGL((attn_valu_kernel<float>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_valu_kernel<bf16_t>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lb

@@ -1,0 +1,108 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels: bf16 storage
+// conversions, MFMA operand types, wavefront reductions and the RoPE angle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lb {
+
+typedef uint16_t bf16_t;  // raw bfloat16 storage
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// scalar conversions (bf16 storage is the upper half of an IEEE binary32)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p) { return Elem<T>::load(p); }
+template <typename T>
+__device__ __forceinline__ void st(T* p, float v) { Elem<T>::store(p, v); }
+
+// Four consecutive elements (16-byte aligned for float, 8-byte for bf16).
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ void load(const float* p, float v[4]) {
+    f32x4 t = *reinterpret_cast<const f32x4*>(p);
+    v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+  }
+  static __device__ __forceinline__ void store(float* p, const float v[4]) {
+    f32x4 t = {v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p) = t;
+  }
+};
+template <> struct Vec4<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float v[4]) {
+    u32x2 t = *reinterpret_cast<const u32x2*>(p);
+    v[0] = __uint_as_float(t[0] << 16); v[1] = __uint_as_float(t[0] & 0xffff0000u);
+    v[2] = __uint_as_float(t[1] << 16); v[3] = __uint_as_float(t[1] & 0xffff0000u);
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float v[4]) {
+    u32x2 t = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<u32x2*>(p) = t;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// wavefront reductions (64 lanes)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// RoPE angle.  phi = pos * inv_freq with inv_freq = theta^(-2k/hd) precomputed
+// in fp64 on the host; the product and its reduction modulo 2*pi are done in
+// fp64 so the angle is accurate to ~1e-13 rad even at positions of 1e5+;
+// sin/cos of the reduced angle are then evaluated in fp32.
+// ---------------------------------------------------------------------------
+struct RopeTable {
+  double inv_freq[128];  // k = 0 .. hd/2-1 (hd <= 256)
+};
+
+__device__ __forceinline__ void rope_sincos(int pos, double inv_freq, float* s, float* c) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double ang = static_cast<double>(pos) * inv_freq;
+  double red = ang - two_pi * rint(ang * (1.0 / two_pi));
+  sincosf(static_cast<float>(red), s, c);
+}
+
+}  // namespace lb

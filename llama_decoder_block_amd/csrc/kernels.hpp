@@ -1,0 +1,203 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace lb {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+inline size_t dtype_bytes(DType t) { return t == DType::F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------
+// GEMM operand description.  The weight operand is a logical [N, K] matrix
+// (row-major, K contiguous) assembled from up to three row segments stored
+// in separate buffers: logical row n in [start[i], start[i+1]) lives at
+// ptr[i] + (n - start[i]) * K.  Q/K/V projections use three segments; the
+// fused gate/up projection uses two (gate rows then up rows).
+// ---------------------------------------------------------------------------
+struct WSeg {
+  const void* ptr[3];
+  int start[4];  // start[nseg] == N
+  int nseg;
+};
+
+// ---------------------------------------------------------------------------
+// Epilogues.  A GEMM computes acc[m][n] = sum_k X[m][k] * W[n][k] in fp32 and
+// hands each output row m four consecutive columns n..n+3 (n % 4 == 0,
+// `cnt` of them valid) to the epilogue.  For the fused gate/up product the
+// epilogue receives the gate and up accumulators of the same column c.
+// ---------------------------------------------------------------------------
+
+// out[m, n] = acc (stored in TO)
+template <typename TO>
+struct EpiStore {
+  TO* out;
+  int ldo;
+  __device__ __forceinline__ void operator()(int m, int n, const float v[4], int cnt) const {
+    TO* p = out + static_cast<int64_t>(m) * ldo + n;
+    if (cnt == 4 && (ldo & 3) == 0) {
+      Vec4<TO>::store(p, v);
+    } else {
+      for (int i = 0; i < cnt; ++i) st(p + i, v[i]);
+    }
+  }
+};
+
+// out[m, n] = resid[m, n] + acc   (residual stream in TR; out may alias resid)
+template <typename TR>
+struct EpiResid {
+  TR* out;
+  const TR* resid;
+  int ldo;
+  __device__ __forceinline__ void operator()(int m, int n, const float v[4], int cnt) const {
+    const int64_t off = static_cast<int64_t>(m) * ldo + n;
+    if (cnt == 4 && (ldo & 3) == 0) {
+      float r[4], o[4];
+      Vec4<TR>::load(resid + off, r);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = r[i] + v[i];
+      Vec4<TR>::store(out + off, o);
+    } else {
+      for (int i = 0; i < cnt; ++i) st(out + off + i, ld(resid + off + i) + v[i]);
+    }
+  }
+};
+
+// Q/K/V projection epilogue: RoPE on the Q and K columns (adjacent pairs
+// (2k, 2k+1) of each head rotated by pos * theta^(-2k/hd)), then the stores:
+// Q to q[m, :]; K and V either to k/v[m, :] (no cache) or to the caches at
+// slot positions[m] of sequence m / seq_len.
+template <typename T>
+struct EpiQkv {
+  T* q;
+  T* k;            // [M, nkv_hd] when kv_cap == 0, else cache [B, kv_cap, nkv_hd]
+  T* v;
+  const int32_t* positions;
+  int nq_hd, nkv_hd, hd, seq_len, kv_cap;
+  RopeTable rope;
+
+  __device__ __forceinline__ void pair(int m, int n, float a, float b) const {
+    const int pos = positions[m];
+    T* dst;
+    if (n < nq_hd + nkv_hd) {
+      const int kidx = (n % hd) >> 1;
+      float s, c;
+      rope_sincos(pos, rope.inv_freq[kidx], &s, &c);
+      const float ra = a * c - b * s;
+      const float rb = a * s + b * c;
+      a = ra;
+      b = rb;
+    }
+    if (n < nq_hd) {
+      dst = q + static_cast<int64_t>(m) * nq_hd + n;
+    } else {
+      const int nn = n < nq_hd + nkv_hd ? n - nq_hd : n - nq_hd - nkv_hd;
+      T* base = n < nq_hd + nkv_hd ? k : v;
+      int64_t row = m;
+      if (kv_cap > 0) {
+        const int bseq = m / seq_len;
+        row = static_cast<int64_t>(bseq) * kv_cap + pos;
+      }
+      dst = base + row * nkv_hd + nn;
+    }
+    st(dst, a);
+    st(dst + 1, b);
+  }
+  __device__ __forceinline__ void operator()(int m, int n, const float v4[4], int cnt) const {
+    if (cnt >= 2) pair(m, n, v4[0], v4[1]);
+    if (cnt >= 4) pair(m, n + 2, v4[2], v4[3]);
+  }
+};
+
+// SwiGLU product: out[m, c] = SiLU(gate) * up with SiLU(z) = z / (1 + e^-z)
+template <typename TO>
+struct EpiSilu {
+  TO* out;
+  int ldo;
+  __device__ __forceinline__ static float silu(float z) { return z / (1.0f + __expf(-z)); }
+  __device__ __forceinline__ void operator()(int m, int c, const float g[4], const float u[4],
+                                             int cnt) const {
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = silu(g[i]) * u[i];
+    TO* p = out + static_cast<int64_t>(m) * ldo + c;
+    if (cnt == 4 && (ldo & 3) == 0) {
+      Vec4<TO>::store(p, o);
+    } else {
+      for (int i = 0; i < cnt; ++i) st(p + i, o[i]);
+    }
+  }
+};
+
+// Raw fp32 partial sums of one K-split: part[z][m][n]
+struct EpiPartial {
+  float* part;
+  int ldo;
+  int64_t split_stride;  // elements between consecutive splits
+  __device__ __forceinline__ void operator()(int m, int n, const float v[4], int cnt) const {
+    float* p = part + blockIdx.z * split_stride + static_cast<int64_t>(m) * ldo + n;
+    if (cnt == 4 && (ldo & 3) == 0) {
+      Vec4<float>::store(p, v);
+    } else {
+      for (int i = 0; i < cnt; ++i) p[i] = v[i];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// GEMM front end: chooses the MFMA kernel (bf16, K % 8 == 0), possibly with a
+// K-split and a reduction pass for few rows, or the generic VALU kernel.
+// ---------------------------------------------------------------------------
+enum class EpiKind { Store, Resid, Qkv, Silu };
+
+struct GemmEpi {
+  EpiKind kind;
+  DType out_dt;        // Store: dtype of out; Resid: residual dtype
+  void* out;
+  const void* resid;
+  int ldo;
+  // Qkv
+  void* q; void* k; void* v;
+  const int32_t* positions;
+  int nq_hd, nkv_hd, hd, seq_len, kv_cap;
+  const RopeTable* rope;
+};
+
+// Workspace bytes the GEMM needs for a given problem (split-K partials).
+size_t gemm_workspace_bytes(DType dt, int M, int N, int K, bool dual);
+
+hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int N, bool dual,
+                       const GemmEpi& epi, void* ws, size_t ws_bytes, hipStream_t s,
+                       const char** kernel_name);
+
+// ---------------------------------------------------------------------------
+// Other launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_rmsnorm(const void* x, const void* res, const void* gamma, void* out,
+                          void* sum_out, int64_t rows, int d, float eps, DType wdt, DType rdt,
+                          hipStream_t s);
+
+hipError_t launch_rope(void* q, void* k, const int32_t* positions, int64_t n_tokens, int nq,
+                       int nkv, int hd, const RopeTable& rope, DType dt, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;       // [B, Tq, nq, hd]
+  const void* k;       // [B, S, nkv, hd]
+  const void* v;
+  void* out;           // [B, Tq, nq, hd]
+  const int32_t* positions;  // [B, Tq] or null (query t sees 0..t)
+  int B, Tq, S, nq, nkv, hd;
+  float scale;         // 1/sqrt(hd)
+};
+
+size_t attention_workspace_bytes(DType dt, int B, int Tq, int S, int nq, int nkv, int hd);
+
+hipError_t launch_attention(DType dt, const AttnArgs& a, void* ws, size_t ws_bytes,
+                            hipStream_t s, const char** kernel_name);
+
+}  // namespace lb
