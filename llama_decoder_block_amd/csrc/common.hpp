@@ -98,11 +98,47 @@ struct RopeTable {
   double inv_freq[128];  // k = 0 .. hd/2-1 (hd <= 256)
 };
 
+// Angle reduction in fp64: phi = pos * inv_freq is formed and reduced to
+// [-1/2, 1/2] revolutions exactly enough (~1e-16 relative) for any int32
+// position; the reduced angle then has an fp32 error of ~2e-7 rad.
+__device__ __forceinline__ float rope_revolutions(int pos, double inv_freq) {
+  const double inv_two_pi = 0.15915494309189533576888376337251;
+  const double rev = static_cast<double>(pos) * inv_freq * inv_two_pi;
+  return static_cast<float>(rev - rint(rev));
+}
+
+// Accurate sin/cos (fp32 outputs).
 __device__ __forceinline__ void rope_sincos(int pos, double inv_freq, float* s, float* c) {
-  const double two_pi = 6.283185307179586476925286766559;
-  double ang = static_cast<double>(pos) * inv_freq;
-  double red = ang - two_pi * rint(ang * (1.0 / two_pi));
-  sincosf(static_cast<float>(red), s, c);
+  const float r = rope_revolutions(pos, inv_freq) * 6.2831853071795865f;
+  sincosf(r, s, c);
+}
+
+// Hardware sin/cos of the reduced angle (v_sin_f32 / v_cos_f32 take
+// revolutions); their error is far below half a bf16 ulp, so they serve
+// every bf16 output.
+__device__ __forceinline__ void rope_sincos_fast(int pos, double inv_freq, float* s, float* c) {
+  const float r = rope_revolutions(pos, inv_freq);
+  *s = __builtin_amdgcn_sinf(r);
+  *c = __builtin_amdgcn_cosf(r);
+}
+
+template <typename T>
+__device__ __forceinline__ void rope_sincos_t(int pos, double inv_freq, float* s, float* c) {
+  if constexpr (sizeof(T) == 2)
+    rope_sincos_fast(pos, inv_freq, s, c);
+  else
+    rope_sincos(pos, inv_freq, s, c);
+}
+
+// SiLU(z) = z / (1 + e^-z).  For bf16 outputs the hardware exp2 and
+// reciprocal (about 1 fp32 ulp each) replace the IEEE-accurate sequence.
+template <typename TO>
+__device__ __forceinline__ float silu_t(float z) {
+  if constexpr (sizeof(TO) == 2) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+  } else {
+    return z / (1.0f + expf(-z));
+  }
 }
 
 }  // namespace lb

@@ -13,12 +13,14 @@
 //   stay inside a lane.  K is walked in steps of 64 through two LDS buffers;
 //   the next step's global loads are in flight while the current step's
 //   MFMAs run.  LDS rows are 128 B (64 bf16) with the 16-byte chunk index
-//   XOR-swizzled by the row so that fragment reads do not collide in banks.
+//   XOR-swizzled by the row pair so that fragment reads do not collide in banks.
 // gemm_valu_kernel: generic fp32-accumulating kernel for the fp32 path and
 //   for shapes the MFMA kernel does not take (K % 8 != 0).
 // split-K: for few token rows (decode) the MFMA kernel writes fp32 partial
 //   sums per K-slice and splitk_reduce_kernel sums them and applies the
 //   epilogue, so enough workgroups stream the weights.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -74,8 +76,15 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int 
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;
 
+// LDS tile rows are 128 B (64 bf16 of K).  gfx950 serves a 16-byte-per-lane
+// LDS read 16 lanes (256 B, all 64 banks) at a time; a fragment read has 16
+// consecutive lanes on 16 consecutive rows at the same K chunk, and each pair
+// of rows shares one 256-B bank line.  XOR-ing the chunk index with
+// (row / 2) % 8 gives the 8 row pairs 8 distinct chunks, so the 16 lanes hit
+// 16 distinct 16-byte bank groups.  The row-major tile stores (8 lanes per
+// row) stay conflict-free under the same map.
 __device__ __forceinline__ int lds_idx(int row, int chunk) {  // in 16-byte units
-  return row * 8 + (chunk ^ (row & 7));
+  return row * 8 + (chunk ^ ((row >> 1) & 7));
 }
 
 template <int BN, int BM, bool DUAL, class Epi>
@@ -218,6 +227,170 @@ gemm_mfma_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, in
 }
 
 // ---------------------------------------------------------------------------
+// MFMA kernel, large tiles: 256 x 256 output tile, eight wavefronts (two per
+// SIMD, so one wavefront's LDS and memory waits overlap the other's MFMAs).
+// Wave grid 2 (N) x 4 (M); each wavefront owns 128 (N) x 64 (M) as 4 x 2
+// tiles of 32 x 32.  Requires K % 64 == 0 (no K tail) so that the global
+// loads of the next K step are issued unconditionally; rows past M or N are
+// clamped on load and dropped by the epilogue.  Fragments of the next
+// 16-wide K slice are read from LDS while the current slice's MFMAs run.
+// ---------------------------------------------------------------------------
+template <bool DUAL, class Epi>
+__global__ void __launch_bounds__(512, 2)
+gemm_mfma8_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, int K,
+                  int tiles_m, int tiles_n, Epi epi) {
+  constexpr int BN = 256, BM = 256;
+  constexpr int WN = 128, WM = 64;
+  constexpr int TN = 4, TM = 2;
+  constexpr int LD_IT = 4;  // 16-byte loads per thread per operand per K step
+  __shared__ u32x4 lds[2][(BN + BM) * 8];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wave_n = wid & 1, wave_m = wid >> 1;
+  const int out_n0 = tn * (DUAL ? BN / 2 : BN);
+  const int m0 = tm * BM;
+  const int KT = K / kBK;
+
+  const int chunk = tid & 7, rbase = tid >> 3;  // rows rbase + 64 i
+  const bf16_t* wsrc[LD_IT];
+  const bf16_t* xsrc[LD_IT];
+#pragma unroll
+  for (int i = 0; i < LD_IT; ++i) {
+    const int r = rbase + 64 * i;
+    const bf16_t* p;
+    if constexpr (DUAL) {
+      // LDS rows [0,128): wave_n 0 (gate 0..63, up 0..63); [128,256): wave_n 1
+      const int wv = r / WN, rr = r % WN;
+      const bool up = rr >= WN / 2;
+      const int c = min(out_n0 + wv * (WN / 2) + (rr % (WN / 2)), N - 1);
+      p = (up ? W.p[1] : W.p[0]) + static_cast<int64_t>(c) * W.ld;
+    } else {
+      p = W.row(min(out_n0 + r, N - 1));
+    }
+    wsrc[i] = p + chunk * 8;
+    xsrc[i] = X + static_cast<int64_t>(min(m0 + r, M - 1)) * K + chunk * 8;
+  }
+
+  // two register staging sets: the loads of K steps kt+1 and kt+2 are in
+  // flight while step kt computes (hides memory latency of ~2 K steps)
+  u32x4 wreg[2][LD_IT], xreg[2][LD_IT];
+  auto gload = [&](int kt, auto S) {
+    constexpr int st = decltype(S)::value;
+#pragma unroll
+    for (int i = 0; i < LD_IT; ++i) wreg[st][i] = *reinterpret_cast<const u32x4*>(wsrc[i] + kt * kBK);
+#pragma unroll
+    for (int i = 0; i < LD_IT; ++i) xreg[st][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kt * kBK);
+  };
+  auto lstore = [&](int buf, auto S) {
+    constexpr int st = decltype(S)::value;
+#pragma unroll
+    for (int i = 0; i < LD_IT; ++i) lds[buf][lds_idx(rbase + 64 * i, chunk)] = wreg[st][i];
+#pragma unroll
+    for (int i = 0; i < LD_IT; ++i) lds[buf][BN * 8 + lds_idx(rbase + 64 * i, chunk)] = xreg[st][i];
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  int arow[TN], brow[TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a) arow[a] = wave_n * WN + a * 32 + frag_row;
+#pragma unroll
+  for (int b = 0; b < TM; ++b) brow[b] = BN + wave_m * WM + b * 32 + frag_row;
+
+  auto compute = [&](int buf) {
+    bf16x8 af[2][TN], bf[2][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+      af[0][a] = __builtin_bit_cast(bf16x8, lds[buf][lds_idx(arow[a], frag_half)]);
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+      bf[0][b] = __builtin_bit_cast(bf16x8, lds[buf][lds_idx(brow[b], frag_half)]);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < kBK / 16) {
+        const int ch = (kk + 1) * 2 + frag_half;
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+          af[cur ^ 1][a] = __builtin_bit_cast(bf16x8, lds[buf][lds_idx(arow[a], ch)]);
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+          bf[cur ^ 1][b] = __builtin_bit_cast(bf16x8, lds[buf][lds_idx(brow[b], ch)]);
+      }
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][a], bf[cur][b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  // K steps in pairs so that staging set and LDS buffer indices are static:
+  // even steps compute LDS buffer 0 / refill set 0, odd steps buffer 1 / set 1.
+  gload(0, S0{});
+  if (KT > 1) gload(1, S1{});
+  lstore(0, S0{});
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    if (kt + 2 < KT) gload(kt + 2, S0{});
+    compute(0);
+    lstore(1, S1{});
+    __syncthreads();
+    if (kt + 3 < KT) gload(kt + 3, S1{});
+    compute(1);
+    if (kt + 2 < KT) lstore(0, S0{});
+    __syncthreads();
+  }
+  if (kt < KT) compute(0);
+
+#pragma unroll
+  for (int b = 0; b < TM; ++b) {
+    const int m = m0 + wave_m * WM + b * 32 + frag_row;
+    if (m >= M) continue;
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int a = 0; a < TN / 2; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = out_n0 + wave_n * (WN / 2) + a * 32 + j * 8 + frag_half * 4;
+          if (c >= N) continue;
+          float g[4], u[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            g[i] = acc[a][b][j * 4 + i];
+            u[i] = acc[a + TN / 2][b][j * 4 + i];
+          }
+          epi(m, c, g, u, min(4, N - c));
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4;
+          if (n >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
+          epi(m, n, v, min(4, N - n));
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Generic VALU kernel (fp32 accumulation), 64x64 tile, 4x4 outputs per thread
 // ---------------------------------------------------------------------------
 template <typename T, bool DUAL, class Epi>
@@ -316,6 +489,7 @@ splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t split_s
 // ---------------------------------------------------------------------------
 struct Plan {
   bool mfma;
+  bool big;       // 256x256 eight-wave kernel
   int bn, bm;     // MFMA tile (bn = weight rows per tile incl. both halves when dual)
   int splits;     // K splits (>1: partial sums + reduce)
   int k_per_split;
@@ -332,6 +506,7 @@ Plan make_plan(DType dt, int M, int N, int K, bool dual) {
   if (M >= 512) {
     p.bn = 256;
     p.bm = 256;
+    p.big = K % kBK == 0;
     return p;
   }
   // few rows (decode): 64x64 tiles; split K until there are >= 512 workgroups
@@ -438,6 +613,22 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
   auto rows = make_rows<bf16_t>(W, K);
   if (p.splits <= 1) {
     if (kernel_name) *kernel_name = dual ? "gemm_mfma_gate_up_silu" : "gemm_mfma";
+    if (p.big) {
+      const int tiles_m = ceil_div(M, 256);
+      const int tiles_n = ceil_div(N, dual ? 128 : 256);
+      dim3 grid(tiles_m * tiles_n);
+      if (dual)
+        return with_silu(epi, [&](auto e) {
+          hipLaunchKernelGGL((gemm_mfma8_kernel<true, decltype(e)>), grid, dim3(512), 0, s, xp, rows, M, N, K,
+                             tiles_m, tiles_n, e);
+          return hipGetLastError();
+        });
+      return with_epi(epi, [&](auto e) {
+        hipLaunchKernelGGL((gemm_mfma8_kernel<false, decltype(e)>), grid, dim3(512), 0, s, xp, rows, M, N, K,
+                           tiles_m, tiles_n, e);
+        return hipGetLastError();
+      });
+    }
     if (p.bn == 256 && p.bm == 256) {
       if (dual)
         return with_silu(epi, [&](auto e) {

@@ -81,36 +81,39 @@ struct EpiQkv {
   int nq_hd, nkv_hd, hd, seq_len, kv_cap;
   RopeTable rope;
 
-  __device__ __forceinline__ void pair(int m, int n, float a, float b) const {
-    const int pos = positions[m];
-    T* dst;
-    if (n < nq_hd + nkv_hd) {
-      const int kidx = (n % hd) >> 1;
+  __device__ __forceinline__ T* dest(int m, int n, int pos) const {
+    if (n < nq_hd) return q + static_cast<int64_t>(m) * nq_hd + n;
+    const bool is_k = n < nq_hd + nkv_hd;
+    const int nn = is_k ? n - nq_hd : n - nq_hd - nkv_hd;
+    int64_t row = m;
+    if (kv_cap > 0) row = static_cast<int64_t>(m / seq_len) * kv_cap + pos;
+    return (is_k ? k : v) + row * nkv_hd + nn;
+  }
+  __device__ __forceinline__ void rotate(int n, int pos, float& a, float& b) const {
+    if (n < nq_hd + nkv_hd) {  // Q or K: rotate the pair; V is stored as is
       float s, c;
-      rope_sincos(pos, rope.inv_freq[kidx], &s, &c);
+      rope_sincos_t<T>(pos, rope.inv_freq[(n % hd) >> 1], &s, &c);
       const float ra = a * c - b * s;
-      const float rb = a * s + b * c;
+      b = a * s + b * c;
       a = ra;
-      b = rb;
     }
-    if (n < nq_hd) {
-      dst = q + static_cast<int64_t>(m) * nq_hd + n;
-    } else {
-      const int nn = n < nq_hd + nkv_hd ? n - nq_hd : n - nq_hd - nkv_hd;
-      T* base = n < nq_hd + nkv_hd ? k : v;
-      int64_t row = m;
-      if (kv_cap > 0) {
-        const int bseq = m / seq_len;
-        row = static_cast<int64_t>(bseq) * kv_cap + pos;
-      }
-      dst = base + row * nkv_hd + nn;
-    }
-    st(dst, a);
-    st(dst + 1, b);
   }
   __device__ __forceinline__ void operator()(int m, int n, const float v4[4], int cnt) const {
-    if (cnt >= 2) pair(m, n, v4[0], v4[1]);
-    if (cnt >= 4) pair(m, n + 2, v4[2], v4[3]);
+    const int pos = positions[m];
+    float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+    if (cnt == 4 && (hd & 3) == 0) {
+      // four columns in one head of one segment: one 4-wide store
+      rotate(n, pos, v[0], v[1]);
+      rotate(n + 2, pos, v[2], v[3]);
+      Vec4<T>::store(dest(m, n, pos), v);
+      return;
+    }
+    for (int pr = 0; pr + 1 < cnt; pr += 2) {
+      rotate(n + pr, pos, v[pr], v[pr + 1]);
+      T* d = dest(m, n + pr, pos);
+      st(d, v[pr]);
+      st(d + 1, v[pr + 1]);
+    }
   }
 };
 
@@ -119,12 +122,11 @@ template <typename TO>
 struct EpiSilu {
   TO* out;
   int ldo;
-  __device__ __forceinline__ static float silu(float z) { return z / (1.0f + __expf(-z)); }
   __device__ __forceinline__ void operator()(int m, int c, const float g[4], const float u[4],
                                              int cnt) const {
     float o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = silu(g[i]) * u[i];
+    for (int i = 0; i < 4; ++i) o[i] = silu_t<TO>(g[i]) * u[i];
     TO* p = out + static_cast<int64_t>(m) * ldo + c;
     if (cnt == 4 && (ldo & 3) == 0) {
       Vec4<TO>::store(p, o);

@@ -31,7 +31,7 @@ rope_kernel(T* __restrict__ x, const int32_t* __restrict__ positions, int64_t n_
   for (int pr = 0; pr < 2; ++pr) {
     const int kidx = ((col + 2 * pr) % hd) >> 1;
     float s, c;
-    rope_sincos(pos, rope.inv_freq[kidx], &s, &c);
+    rope_sincos_t<T>(pos, rope.inv_freq[kidx], &s, &c);
     const float a = v[2 * pr], b = v[2 * pr + 1];
     v[2 * pr] = a * c - b * s;
     v[2 * pr + 1] = a * s + b * c;
@@ -52,7 +52,7 @@ rope_pair_kernel(T* __restrict__ x, const int32_t* __restrict__ positions, int64
   const int pos = positions[tok];
   T* p = x + tok * row_len + col;
   float s, c;
-  rope_sincos(pos, rope.inv_freq[(col % hd) >> 1], &s, &c);
+  rope_sincos_t<T>(pos, rope.inv_freq[(col % hd) >> 1], &s, &c);
   const float a = ld(p), b = ld(p + 1);
   st(p, a * c - b * s);
   st(p + 1, a * s + b * c);

@@ -91,7 +91,8 @@ def test_small_block_bf16(kw):
     check_bf16(f"small bf16 {kw}", y, inp)
 
 
-@pytest.mark.parametrize("name,seq", [("llama3_8b_gqa_prefill", 256), ("llama7b_mha_prefill", 160)])
+@pytest.mark.parametrize("name,seq", [("llama3_8b_gqa_prefill", 256), ("llama7b_mha_prefill", 160),
+                                      ("llama3_8b_gqa_prefill", 1100)])
 def test_model_width_block_bf16(name, seq):
     inp = synth.make_block_inputs(synth.workload(name, seq=seq))
     y, _, _ = run_block(inp)

@@ -253,9 +253,9 @@ def test_decode_attention(nq, nkv, hd, dtype):
 @pytest.mark.parametrize("n,d,dff", [(37, 64, 96), (5, 16, 48), (70, 130, 50)])
 def test_swiglu_f32(n, d, dff):
     x = synth.normal(100, (n, d))
-    wg = synth.normal(101, (dff, d), 0.2)
-    wu = synth.normal(102, (dff, d), 0.2)
-    wd = synth.normal(103, (d, dff), 0.2)
+    wg = synth.normal(101, (dff, d), 0.02)
+    wu = synth.normal(102, (dff, d), 0.02)
+    wd = synth.normal(103, (d, dff), 0.02)
     r = synth.normal(104, (n, d))
     out = binding.swiglu_ffn(dev(x), dev(wg), dev(wu), dev(wd), residual=dev(r))
     torch.cuda.synchronize()
