@@ -76,6 +76,19 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int 
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;
 
+#ifndef LB_GEMM_FOUR_WAVES
+#define LB_GEMM_FOUR_WAVES 1
+#endif
+#ifndef LB_GEMM_RS
+#define LB_GEMM_RS 1
+#endif
+#ifndef LB_GEMM_DMA64
+#define LB_GEMM_DMA64 0
+#endif
+#ifndef LB_GEMM_NST
+#define LB_GEMM_NST 4
+#endif
+
 // LDS tile rows are 128 B (64 bf16 of K).  gfx950 serves a 16-byte-per-lane
 // LDS read 16 lanes (256 B, all 64 banks) at a time; a fragment read has 16
 // consecutive lanes on 16 consecutive rows at the same K chunk, and each pair
@@ -391,6 +404,627 @@ gemm_mfma8_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, i
 }
 
 // ---------------------------------------------------------------------------
+// MFMA kernel, large tiles, direct-to-LDS staging ("dma" kernel).
+// 256 x 256 output tile, four wavefronts (one per SIMD) in a 2 x 2 grid, each
+// owning 128 x 128 as 4 x 4 tiles of 32 x 32 (accumulators in AGPRs).
+// K advances in stages of 32.  Global memory is copied straight into LDS by
+// global_load_lds_dwordx4 (lane l of an instruction writes LDS bytes
+// M0 + 16 l .. +15), so no registers stage the tiles; NST stage buffers let
+// the copies of stage kt+NST-1 be issued while stage kt computes.
+// LDS rows are 64 B (32 bf16): chunk c of row r is stored at chunk
+// c ^ ((r / 4) % 4), which keeps the 16 lanes served together by a 16-byte
+// LDS read (16 consecutive rows, one chunk) on 16 distinct bank groups; the
+// copy realises the swizzle by choosing each lane's global chunk.
+// Inside a stage the fragments of the next 16-wide sub-step are read while
+// the current sub-step's 16 MFMAs run, and the first fragments of stage kt+1
+// are read before the end-of-stage barrier (that stage was confirmed complete
+// one barrier earlier), so the barrier does not idle the matrix cores.
+// Requires K % 32 == 0.
+// ---------------------------------------------------------------------------
+constexpr int kDmaBK = 32;
+
+__device__ __forceinline__ int dma_lds_off(int row, int chunk) {  // bytes within a stage operand
+  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <bool DUAL, int NST, class Epi>
+__global__ void __launch_bounds__(256, 1)
+gemm_mfma_dma_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, int K,
+                     int tiles_m, int tiles_n, Epi epi) {
+  constexpr int BN = 256, BM = 256, WN = 128, WM = 128, TN = 4, TM = 4;
+  constexpr int OP_BYTES = 256 * 64;            // one operand of one stage (16 KB)
+  constexpr int STAGE_BYTES = 2 * OP_BYTES;     // weights then activations
+  constexpr int LOADS = 8;                      // DMA instructions per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE_BYTES];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_n = wid & 1, wave_m = wid >> 1;
+  const int out_n0 = tn * (DUAL ? BN / 2 : BN);
+  const int m0 = tm * BM;
+  const int KT = K / kDmaBK;
+
+  // Copy assignment: wave w, instruction j (0..3) fills rows (4w + j)*16 ..
+  // +15 of the weight tile (and, for j in 4..7, of the activation tile).
+  // Lane i covers row +i/4, LDS chunk i%4, i.e. global chunk (i%4)^((row/4)%4).
+  const bf16_t* src[LOADS];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = (wid * 4 + j) * 16 + (lane >> 2);
+    const int gchunk = (lane & 3) ^ ((r >> 2) & 3);
+    const bf16_t* wp;
+    if constexpr (DUAL) {
+      const int wv = r / WN, rr = r % WN;
+      const bool up = rr >= WN / 2;
+      const int c = min(out_n0 + wv * (WN / 2) + (rr % (WN / 2)), N - 1);
+      wp = (up ? W.p[1] : W.p[0]) + static_cast<int64_t>(c) * W.ld;
+    } else {
+      wp = W.row(min(out_n0 + r, N - 1));
+    }
+    src[j] = wp + gchunk * 8;
+    src[4 + j] = X + static_cast<int64_t>(min(m0 + r, M - 1)) * K + gchunk * 8;
+  }
+  auto issue_stage = [&](int kt) {
+    uint8_t* base = lds + (kt % NST) * STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      uint8_t* dst = base + (j >= 4 ? OP_BYTES : 0) + ((wid * 4 + (j & 3)) * 16) * 64;
+      __builtin_amdgcn_global_load_lds(src[j] + kt * kDmaBK, dst, 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  int aoff[TN], boff[TM];
+  bf16x8 fa[2][TN], fb[2][TM];
+  auto read_frags = [&](int kt, int sub, auto F) {
+    constexpr int f = decltype(F)::value;
+    const uint8_t* base = lds + (kt % NST) * STAGE_BYTES;
+    const int ch = sub * 2 + frag_half;
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+      fa[f][a] = *reinterpret_cast<const bf16x8*>(base + dma_lds_off(wave_n * WN + a * 32 + frag_row, ch));
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+      fb[f][b] = *reinterpret_cast<const bf16x8*>(base + OP_BYTES + dma_lds_off(wave_m * WM + b * 32 + frag_row, ch));
+  };
+  (void)aoff; (void)boff;
+  auto mfmas = [&](auto F) {
+    constexpr int f = decltype(F)::value;
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][a], fb[f][b], acc[a][b], 0, 0, 0);
+  };
+  using F0 = std::integral_constant<int, 0>;
+  using F1 = std::integral_constant<int, 1>;
+
+  // MFMAs of one sub-step in two parts so that LDS reads can be issued after
+  // the first few have started
+  auto mfmas_part = [&](auto F, auto LO, auto HI) {
+    constexpr int f = decltype(F)::value;
+    constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
+#pragma unroll
+    for (int t = lo; t < hi; ++t)
+      acc[t / TM][t % TM] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][t / TM], fb[f][t % TM], acc[t / TM][t % TM], 0, 0, 0);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P4 = std::integral_constant<int, 4>;
+  using P16 = std::integral_constant<int, 16>;
+  // Barrier without the implied memory-counter waits of __syncthreads():
+  // the copies of later stages stay in flight across it.  The memory clobber
+  // keeps the compiler from moving LDS accesses across it.
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: stages 0 .. NST-2 in flight; stages 0 and 1 complete
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < KT) issue_stage(s);
+  if (KT >= NST - 1) wait_vmcnt<LOADS * (NST - 3)>();
+  else wait_vmcnt<0>();
+  barrier();
+  read_frags(0, 0, F0{});
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const bool issue = kt + NST - 1 < KT;
+    if (issue) issue_stage(kt + NST - 1);
+    // sub-step 0 (fragments in set 0); read sub-step 1 into set 1
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas_part(F0{}, P0{}, P4{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(kt, 1, F1{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas_part(F0{}, P4{}, P16{});
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 1 (set 1); read sub-step 0 of stage kt+1 into set 0 (that
+    // stage was confirmed complete at the previous barrier)
+    mfmas_part(F1{}, P0{}, P4{});
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < KT) read_frags(kt + 1, 0, F0{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas_part(F1{}, P4{}, P16{});
+    // stage kt+2 complete for this wave (newer stages may stay in flight),
+    // then the barrier publishes it and frees stage kt's buffer
+    if (issue) wait_vmcnt<LOADS * (NST - 3)>();
+    else wait_vmcnt<0>();
+    barrier();
+  }
+
+  // epilogue: register e of a 32x32 tile is feature row (e/4)*8 + half*4 + e%4
+  // of the weight operand and token column lane%32
+#pragma unroll
+  for (int b = 0; b < TM; ++b) {
+    const int m = m0 + wave_m * WM + b * 32 + frag_row;
+    if (m >= M) continue;
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int a = 0; a < TN / 2; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = out_n0 + wave_n * (WN / 2) + a * 32 + j * 8 + frag_half * 4;
+          if (c >= N) continue;
+          float g[4], u[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            g[i] = acc[a][b][j * 4 + i];
+            u[i] = acc[a + TN / 2][b][j * 4 + i];
+          }
+          epi(m, c, g, u, min(4, N - c));
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4;
+          if (n >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
+          epi(m, n, v, min(4, N - n));
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel, large tiles, register-staged buffer loads ("rs" kernel).
+// 256 x 256 output tile, four wavefronts (one per SIMD) in a 2 x 2 grid, each
+// owning 128 x 128 as 4 x 4 tiles of 32 x 32 (accumulators in AGPRs).
+// K advances in steps of 64 so that every global load request covers a whole
+// 128-byte line (8 lanes x 16 B of one row).  The operands are read with
+// buffer loads: one SGPR resource per operand segment and a 32-bit per-lane
+// offset, so rows past M or N come back as zeros from the hardware range
+// check instead of being clamped.  Per K step kt each wavefront
+//   * issues the global loads of step kt+2 into one register staging set,
+//   * writes the staging set holding step kt+1 into the other LDS buffer,
+//   * runs 4 sub-steps of 16 MFMAs, reading the next sub-step's fragments
+//     after the first 4 MFMAs of the current one,
+//   * and crosses the end-of-step barrier half-way through the last
+//     sub-step's MFMAs, then reads the first fragments of step kt+1.
+// Requires K % 64 == 0 and weight-segment boundaries at multiples of 32 rows.
+// ---------------------------------------------------------------------------
+struct BufOperands {
+  const bf16_t* x;        // activations [M, K]
+  const bf16_t* w[3];     // weight segments, each [rows_i, K]
+  int wrows[3];           // rows of each segment (bounds for the range check)
+  int s1, s2;             // logical start rows of segments 1 and 2
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+template <bool DUAL, class Epi>
+__global__ void __launch_bounds__(256, 1)
+gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_n, Epi epi) {
+  constexpr int BN = 256, BM = 256, WN = 128, WM = 128, TN = 4, TM = 4;
+  constexpr int GROUPS = 8;  // row groups of 32 per operand
+  __shared__ u32x4 lds[2][(BN + BM) * 8];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wave_n = wid & 1, wave_m = wid >> 1;
+  const int out_n0 = tn * (DUAL ? BN / 2 : BN);
+  const int m0 = tm * BM;
+  const int KT = K / kBK;
+  const uint32_t row_bytes = static_cast<uint32_t>(K) * 2u;
+  const int chunk = tid & 7, rbase = tid >> 3;
+  const uint32_t voff = static_cast<uint32_t>(rbase) * row_bytes + static_cast<uint32_t>(chunk) * 16u;
+
+  // Each 32-row group of an operand gets its own buffer resource whose base is
+  // the group's first row and whose size ends at the operand's last row, so
+  // the per-lane offset is just (row within group, chunk, K position); rows
+  // past the end read as zero.  The resources are uniform (SALU arithmetic).
+  auto group_rsrc = [&](const bf16_t* base, int first_row, int rows) {
+    const int left = rows - first_row;
+    const uint32_t bytes = left > 0 ? static_cast<uint32_t>(left) * row_bytes : 0u;
+    const bf16_t* p = left > 0 ? base + static_cast<int64_t>(first_row) * K : base;
+    return make_rsrc(p, bytes);
+  };
+  auto w_rsrc = [&](int g) {
+    if constexpr (DUAL) {
+      const int r0 = 32 * g, wv = r0 / WN, rr0 = r0 % WN;
+      const int c0 = out_n0 + wv * (WN / 2) + (rr0 % (WN / 2));
+      return group_rsrc(rr0 >= WN / 2 ? op.w[1] : op.w[0], c0, N);
+    } else {
+      const int n0 = out_n0 + 32 * g;
+      if (n0 < op.s1) return group_rsrc(op.w[0], n0, op.wrows[0]);
+      if (n0 < op.s2) return group_rsrc(op.w[1], n0 - op.s1, op.wrows[1]);
+      return group_rsrc(op.w[2], n0 - op.s2, op.wrows[2]);
+    }
+  };
+
+  u32x4 wreg[2][GROUPS], xreg[2][GROUPS];
+  auto gload = [&](int kt, int g, auto S) {
+    constexpr int st = decltype(S)::value;
+    const uint32_t vo = voff + static_cast<uint32_t>(kt) * (kBK * 2);
+    wreg[st][g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc(g), vo, 0, 0));
+    xreg[st][g] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(group_rsrc(op.x, m0 + 32 * g, M), vo, 0, 0));
+  };
+  auto lstore = [&](int buf, int g, auto S) {
+    constexpr int st = decltype(S)::value;
+    lds[buf][lds_idx(rbase + 32 * g, chunk)] = wreg[st][g];
+    lds[buf][BN * 8 + lds_idx(rbase + 32 * g, chunk)] = xreg[st][g];
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  bf16x8 fa[2][TN], fb[2][TM];
+  auto read_frags = [&](int buf, int sub, auto F) {
+    constexpr int f = decltype(F)::value;
+    const int ch = sub * 2 + frag_half;
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+      fa[f][a] = __builtin_bit_cast(bf16x8, lds[buf][lds_idx(wave_n * WN + a * 32 + frag_row, ch)]);
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+      fb[f][b] = __builtin_bit_cast(bf16x8, lds[buf][BN * 8 + lds_idx(wave_m * WM + b * 32 + frag_row, ch)]);
+  };
+  auto mfmas = [&](auto F, auto LO, auto HI) {
+    constexpr int f = decltype(F)::value;
+    constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
+#pragma unroll
+    for (int t = lo; t < hi; ++t)
+      acc[t / TM][t % TM] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][t / TM], fb[f][t % TM], acc[t / TM][t % TM], 0, 0, 0);
+  };
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto barrier = [&]() {
+    fence();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    fence();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  using I16 = std::integral_constant<int, 16>;
+
+  // one K step on LDS buffer BUF; staging set P holds step kt+1, set Q
+  // receives step kt+2
+  auto kstep = [&](int kt, auto BUFc, auto P, auto Q) {
+    constexpr int buf = decltype(BUFc)::value;
+    // Straight-line on purpose: loads, stores and fragment reads are issued
+    // unconditionally (past the last K step the buffer range check returns
+    // zeros or in-bounds data that is never consumed), so the compiler can
+    // count outstanding loads exactly instead of waiting for the newest ones.
+    // sub-step 0
+    gload(kt + 2, 0, Q);
+    gload(kt + 2, 1, Q);
+    fence();
+    mfmas(I0{}, I0{}, I4{});
+    fence();
+    read_frags(buf, 1, I1{});
+    fence();
+    mfmas(I0{}, I4{}, I16{});
+    fence();
+    // sub-step 1
+    gload(kt + 2, 2, Q);
+    gload(kt + 2, 3, Q);
+    lstore(buf ^ 1, 0, P);
+    lstore(buf ^ 1, 1, P);
+    fence();
+    mfmas(I1{}, I0{}, I4{});
+    fence();
+    read_frags(buf, 2, I0{});
+    fence();
+    mfmas(I1{}, I4{}, I16{});
+    fence();
+    // sub-step 2
+    gload(kt + 2, 4, Q);
+    gload(kt + 2, 5, Q);
+    lstore(buf ^ 1, 2, P);
+    lstore(buf ^ 1, 3, P);
+    fence();
+    mfmas(I0{}, I0{}, I4{});
+    fence();
+    read_frags(buf, 3, I1{});
+    fence();
+    mfmas(I0{}, I4{}, I16{});
+    fence();
+    // sub-step 3, with the end-of-step barrier half-way
+    gload(kt + 2, 6, Q);
+    gload(kt + 2, 7, Q);
+#pragma unroll
+    for (int g = 4; g < GROUPS; ++g) lstore(buf ^ 1, g, P);
+    fence();
+    mfmas(I1{}, I0{}, I8{});
+    barrier();
+    read_frags(buf ^ 1, 0, I0{});
+    fence();
+    mfmas(I1{}, I8{}, I16{});
+    fence();
+  };
+
+  // prologue: step 0 in LDS buffer 0 (staging set 0), step 1 in flight (set 1)
+#pragma unroll
+  for (int g = 0; g < GROUPS; ++g) gload(0, g, I0{});
+#pragma unroll
+  for (int g = 0; g < GROUPS; ++g) gload(1, g, I1{});
+#pragma unroll
+  for (int g = 0; g < GROUPS; ++g) lstore(0, g, I0{});
+  barrier();
+  read_frags(0, 0, I0{});
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    kstep(kt, I0{}, I1{}, I0{});
+    kstep(kt + 1, I1{}, I0{}, I1{});
+  }
+  if (kt < KT) kstep(kt, I0{}, I1{}, I0{});
+
+  // epilogue: register e of a 32x32 tile is feature row (e/4)*8 + half*4 + e%4
+  // of the weight operand and token column lane%32
+#pragma unroll
+  for (int b = 0; b < TM; ++b) {
+    const int m = m0 + wave_m * WM + b * 32 + frag_row;
+    if (m >= M) continue;
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int a = 0; a < TN / 2; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = out_n0 + wave_n * (WN / 2) + a * 32 + j * 8 + frag_half * 4;
+          if (c >= N) continue;
+          float g[4], u[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            g[i] = acc[a][b][j * 4 + i];
+            u[i] = acc[a + TN / 2][b][j * 4 + i];
+          }
+          epi(m, c, g, u, min(4, N - c));
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4;
+          if (n >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
+          epi(m, n, v, min(4, N - n));
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel, large tiles, direct-to-LDS copies of 64-wide K steps
+// ("dma64").  256 x 256 output tile, four wavefronts (one per SIMD), each
+// owning 128 x 128 as 4 x 4 tiles of 32 x 32 with AGPR accumulators.  Each
+// global_load_lds_dwordx4 copies 8 whole 128-byte rows (one cache line each)
+// into LDS, so no registers stage the tiles and the compiler inserts no
+// waits for them: the vmcnt waits below are explicit.  Two 64 KB stage
+// buffers: the copy of step kt+1 is issued as soon as the barrier of step
+// kt-1 frees its buffer and must land before the barrier of step kt.  Inside
+// a step the next 16-wide sub-step's fragments are read after the first 4
+// MFMAs of the current one; the barrier sits half-way through the last
+// sub-step's MFMAs, after which the first fragments of step kt+1 are read.
+// LDS rows are 128 B with the chunk XOR (row/2)%8 (conflict-free reads).
+// Requires K % 64 == 0.
+// ---------------------------------------------------------------------------
+template <bool DUAL, class Epi>
+__global__ void __launch_bounds__(256, 1)
+gemm_mfma_dma64_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, int K,
+                       int tiles_m, int tiles_n, Epi epi) {
+  constexpr int BN = 256, BM = 256, WN = 128, WM = 128, TN = 4, TM = 4;
+  constexpr int OP_BYTES = 256 * 128;           // one operand of one step (32 KB)
+  constexpr int STAGE_BYTES = 2 * OP_BYTES;
+  constexpr int LOADS = 16;                     // copies per wavefront per step
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE_BYTES];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_n = wid & 1, wave_m = wid >> 1;
+  const int out_n0 = tn * (DUAL ? BN / 2 : BN);
+  const int m0 = tm * BM;
+  const int KT = K / kBK;
+
+  // wavefront w, copy j (0..7) fills rows (8w + j)*8 .. +7 of the weight tile
+  // (j+8: of the activation tile); lane i covers row +i/8, LDS chunk i%8,
+  // read from global chunk (i%8) ^ ((row/2)%8).
+  const int rsub = lane >> 3, lchunk = lane & 7;
+  const bf16_t* src[LOADS];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (wid * 8 + j) * 8 + rsub;
+    const int gchunk = lchunk ^ ((r >> 1) & 7);
+    const bf16_t* wp;
+    if constexpr (DUAL) {
+      const int wv = r / WN, rr = r % WN;
+      const bool up = rr >= WN / 2;
+      const int c = min(out_n0 + wv * (WN / 2) + (rr % (WN / 2)), N - 1);
+      wp = (up ? W.p[1] : W.p[0]) + static_cast<int64_t>(c) * W.ld;
+    } else {
+      wp = W.row(min(out_n0 + r, N - 1));
+    }
+    src[j] = wp + gchunk * 8;
+    src[8 + j] = X + static_cast<int64_t>(min(m0 + r, M - 1)) * K + gchunk * 8;
+  }
+  auto issue_step = [&](int kt) {
+    uint8_t* base = lds + (kt & 1) * STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      uint8_t* dst = base + (j >= 8 ? OP_BYTES : 0) + ((wid * 8 + (j & 7)) * 8) * 128;
+      __builtin_amdgcn_global_load_lds(src[j] + kt * kBK, dst, 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  bf16x8 fa[2][TN], fb[2][TM];
+  auto read_frags = [&](int kt, int sub, auto F) {
+    constexpr int f = decltype(F)::value;
+    const uint8_t* base = lds + (kt & 1) * STAGE_BYTES;
+    const int ch = sub * 2 + frag_half;
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+      const int r = wave_n * WN + a * 32 + frag_row;
+      fa[f][a] = *reinterpret_cast<const bf16x8*>(base + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
+    }
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      const int r = wave_m * WM + b * 32 + frag_row;
+      fb[f][b] = *reinterpret_cast<const bf16x8*>(base + OP_BYTES + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
+    }
+  };
+  auto mfmas = [&](auto F, auto LO, auto HI) {
+    constexpr int f = decltype(F)::value;
+    constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
+#pragma unroll
+    for (int t = lo; t < hi; ++t)
+      acc[t / TM][t % TM] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][t / TM], fb[f][t % TM], acc[t / TM][t % TM], 0, 0, 0);
+  };
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  // explicit waits: copies (vmcnt) and this wave's LDS reads (lgkmcnt), then
+  // a barrier without the compiler-implied full memory drain
+  auto barrier = [&]() {
+    fence();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    fence();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  using I16 = std::integral_constant<int, 16>;
+
+  issue_step(0);
+  barrier();
+  read_frags(0, 0, I0{});
+  for (int kt = 0; kt < KT; ++kt) {
+    const bool more = kt + 1 < KT;
+    if (more) issue_step(kt + 1);
+    fence();
+    mfmas(I0{}, I0{}, I4{});
+    fence();
+    read_frags(kt, 1, I1{});
+    fence();
+    mfmas(I0{}, I4{}, I16{});
+    fence();
+    mfmas(I1{}, I0{}, I4{});
+    fence();
+    read_frags(kt, 2, I0{});
+    fence();
+    mfmas(I1{}, I4{}, I16{});
+    fence();
+    mfmas(I0{}, I0{}, I4{});
+    fence();
+    read_frags(kt, 3, I1{});
+    fence();
+    mfmas(I0{}, I4{}, I16{});
+    fence();
+    mfmas(I1{}, I0{}, I8{});
+    barrier();
+    if (more) read_frags(kt + 1, 0, I0{});
+    fence();
+    mfmas(I1{}, I8{}, I16{});
+    fence();
+  }
+
+  // epilogue: register e of a 32x32 tile is feature row (e/4)*8 + half*4 + e%4
+  // of the weight operand and token column lane%32
+#pragma unroll
+  for (int b = 0; b < TM; ++b) {
+    const int m = m0 + wave_m * WM + b * 32 + frag_row;
+    if (m >= M) continue;
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int a = 0; a < TN / 2; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = out_n0 + wave_n * (WN / 2) + a * 32 + j * 8 + frag_half * 4;
+          if (c >= N) continue;
+          float g[4], u[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            g[i] = acc[a][b][j * 4 + i];
+            u[i] = acc[a + TN / 2][b][j * 4 + i];
+          }
+          epi(m, c, g, u, min(4, N - c));
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4;
+          if (n >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
+          epi(m, n, v, min(4, N - n));
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Generic VALU kernel (fp32 accumulation), 64x64 tile, 4x4 outputs per thread
 // ---------------------------------------------------------------------------
 template <typename T, bool DUAL, class Epi>
@@ -562,6 +1196,34 @@ hipError_t launch_mfma(const bf16_t* X, const WRows<bf16_t>& W, int M, int N, in
   return hipGetLastError();
 }
 
+
+// The buffer-load kernel needs every 32-row group of a tile inside one weight
+// segment and byte offsets that fit in 32 bits.
+bool rs_ok(const WSeg& w, int N, bool dual) {
+  for (int i = 1; i < w.nseg; ++i)
+    if (w.start[i] % 32 != 0) return false;
+  (void)dual;
+  (void)N;
+  return true;
+}
+
+BufOperands buf_operands(const bf16_t* x, const WSeg& w, int N, bool dual) {
+  BufOperands op{};
+  op.x = x;
+  for (int i = 0; i < 3; ++i) op.w[i] = static_cast<const bf16_t*>(w.ptr[i < w.nseg ? i : 0]);
+  if (dual) {
+    op.wrows[0] = N;
+    op.wrows[1] = N;
+    op.wrows[2] = 0;
+    op.s1 = op.s2 = 0x7fffffff;
+  } else {
+    for (int i = 0; i < 3; ++i) op.wrows[i] = i < w.nseg ? w.start[i + 1] - w.start[i] : 0;
+    op.s1 = w.nseg > 1 ? w.start[1] : 0x7fffffff;
+    op.s2 = w.nseg > 2 ? w.start[2] : 0x7fffffff;
+  }
+  return op;
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(DType dt, int M, int N, int K, bool dual) {
@@ -613,6 +1275,55 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
   auto rows = make_rows<bf16_t>(W, K);
   if (p.splits <= 1) {
     if (kernel_name) *kernel_name = dual ? "gemm_mfma_gate_up_silu" : "gemm_mfma";
+    if (p.big && LB_GEMM_DMA64) {
+      const int tiles_m = ceil_div(M, 256);
+      const int tiles_n = ceil_div(N, dual ? 128 : 256);
+      dim3 grid(tiles_m * tiles_n);
+      if (dual)
+        return with_silu(epi, [&](auto e) {
+          hipLaunchKernelGGL((gemm_mfma_dma64_kernel<true, decltype(e)>), grid, dim3(256), 0, s, xp, rows, M, N,
+                             K, tiles_m, tiles_n, e);
+          return hipGetLastError();
+        });
+      return with_epi(epi, [&](auto e) {
+        hipLaunchKernelGGL((gemm_mfma_dma64_kernel<false, decltype(e)>), grid, dim3(256), 0, s, xp, rows, M, N, K,
+                           tiles_m, tiles_n, e);
+        return hipGetLastError();
+      });
+    }
+    if (p.big && LB_GEMM_RS && rs_ok(W, N, dual)) {
+      const int tiles_m = ceil_div(M, 256);
+      const int tiles_n = ceil_div(N, dual ? 128 : 256);
+      dim3 grid(tiles_m * tiles_n);
+      BufOperands op = buf_operands(xp, W, N, dual);
+      if (dual)
+        return with_silu(epi, [&](auto e) {
+          hipLaunchKernelGGL((gemm_mfma_rs_kernel<true, decltype(e)>), grid, dim3(256), 0, s, op, M, N, K,
+                             tiles_m, tiles_n, e);
+          return hipGetLastError();
+        });
+      return with_epi(epi, [&](auto e) {
+        hipLaunchKernelGGL((gemm_mfma_rs_kernel<false, decltype(e)>), grid, dim3(256), 0, s, op, M, N, K,
+                           tiles_m, tiles_n, e);
+        return hipGetLastError();
+      });
+    }
+    if (p.big && LB_GEMM_FOUR_WAVES) {
+      const int tiles_m = ceil_div(M, 256);
+      const int tiles_n = ceil_div(N, dual ? 128 : 256);
+      dim3 grid(tiles_m * tiles_n);
+      if (dual)
+        return with_silu(epi, [&](auto e) {
+          hipLaunchKernelGGL((gemm_mfma_dma_kernel<true, LB_GEMM_NST, decltype(e)>), grid, dim3(256), 0, s, xp, rows, M, N, K,
+                             tiles_m, tiles_n, e);
+          return hipGetLastError();
+        });
+      return with_epi(epi, [&](auto e) {
+        hipLaunchKernelGGL((gemm_mfma_dma_kernel<false, LB_GEMM_NST, decltype(e)>), grid, dim3(256), 0, s, xp, rows, M, N, K,
+                           tiles_m, tiles_n, e);
+        return hipGetLastError();
+      });
+    }
     if (p.big) {
       const int tiles_m = ceil_div(M, 256);
       const int tiles_n = ceil_div(N, dual ? 128 : 256);
