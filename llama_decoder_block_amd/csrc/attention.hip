@@ -31,6 +31,7 @@ namespace lb {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.0f;  // lazy-rescale threshold of the flash kernel (log2 units)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -165,17 +166,35 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
   const int k_chunk = tid & 15, k_row = tid >> 4;     // rows k_row + 16 i
   const int v_kg = tid & 15, v_hc = tid >> 4;         // slots 4*v_kg..+3, hd 8*v_hc..+7
   u32x4 kreg[4], vreg[4];
+  // lane offsets (elements) of this thread's K rows / V slots within a tile
+  int koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = (k_row + 16 * i) * static_cast<int>(kvrow) + k_chunk * 8;
+    voff[i] = (4 * v_kg + i) * static_cast<int>(kvrow) + v_hc * 8;
+  }
   auto gload = [&](int kt) {
     const int base = kt * kFKeys;
+    if (base + kFKeys <= a.S) {
+      // whole tile inside the cache: uniform tile base + lane offsets
+      const bf16_t* kt_k = kbase + static_cast<int64_t>(base) * kvrow;
+      const bf16_t* kt_v = vbase + static_cast<int64_t>(base) * kvrow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = min(base + k_row + 16 * i, a.S - 1);
-      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + j * kvrow + k_chunk * 8);
-    }
+      for (int i = 0; i < 4; ++i) kreg[i] = *reinterpret_cast<const u32x4*>(kt_k + koff[i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = min(base + 4 * v_kg + i, a.S - 1);
-      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + j * kvrow + v_hc * 8);
+      for (int i = 0; i < 4; ++i) vreg[i] = *reinterpret_cast<const u32x4*>(kt_v + voff[i]);
+    } else {
+      // last, partial tile: clamp slots to the cache (masked anyway)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = min(base + k_row + 16 * i, a.S - 1);
+        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + j * kvrow + k_chunk * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = min(base + 4 * v_kg + i, a.S - 1);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + j * kvrow + v_hc * 8);
+      }
     }
   };
   auto lstore = [&](int buf) {
@@ -184,17 +203,16 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<u32x4*>(kb + (k_row + 16 * i) * kKStride + k_chunk * 16) = kreg[i];
-    // transpose 4 slots x 8 hd into 8 rows (hd) of 4 slots
+    // transpose 4 slots x 8 hd into 8 rows (hd) of 4 slots: output word
+    // (slot pair, hd e) takes the same 16-bit half of two input words
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int word = e >> 1;
-      const bool hi = e & 1;
-      uint32_t s0 = hi ? (vreg[0][word] >> 16) : (vreg[0][word] & 0xffffu);
-      uint32_t s1 = hi ? (vreg[1][word] >> 16) : (vreg[1][word] & 0xffffu);
-      uint32_t s2 = hi ? (vreg[2][word] >> 16) : (vreg[2][word] & 0xffffu);
-      uint32_t s3 = hi ? (vreg[3][word] >> 16) : (vreg[3][word] & 0xffffu);
-      u32x2 pk = {s0 | (s1 << 16), s2 | (s3 << 16)};
-      *reinterpret_cast<u32x2*>(vb + (v_hc * 8 + e) * kVStride + v_kg * 8) = pk;
+    for (int w = 0; w < 4; ++w) {
+      const u32x2 lo = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u),
+                        __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u),
+                        __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u)};
+      *reinterpret_cast<u32x2*>(vb + (v_hc * 8 + 2 * w) * kVStride + v_kg * 8) = lo;
+      *reinterpret_cast<u32x2*>(vb + (v_hc * 8 + 2 * w + 1) * kVStride + v_kg * 8) = hi;
     }
   };
 
@@ -218,38 +236,54 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
     const uint8_t* vb = kb + kKBytes;
 
     // S^T = K Q^T for two 32-slot halves
+    // the two 32-slot halves alternate so consecutive MFMAs are independent
     f32x16 sacc[2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
             kb + (h2 * 32 + (lane & 31)) * kKStride + kk * 32 + half * 16);
         sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[h2], 0, 0, 0);
       }
-    }
-    // scale, mask, running max
+    // Raw-score maximum of the tile (the scale c > 0 preserves order); keys
+    // past a query's position are masked only on tiles that reach the
+    // diagonal of some row of this wavefront (wave-uniform test).
     const bool need_mask = kt * kFKeys + kFKeys - 1 > wave_min;
+    if (need_mask) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = kt * kFKeys + h2 * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          if (j > my_vis) sacc[h2][e] = -INFINITY;
+        }
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float s = sacc[h2][e] * c;
-        if (need_mask) {
-          const int j = kt * kFKeys + h2 * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-          if (j > my_vis) s = -INFINITY;
-        }
-        sacc[h2][e] = s;
-        tmax = fmaxf(tmax, s);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[h2][e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
+    // Lazy rescaling: the reference maximum m_run only moves when a row's
+    // tile maximum exceeds it by more than kRescale (log2 units), so most
+    // tiles skip rescaling O and l.  Any reference gives the same softmax;
+    // the weights stay <= 2^kRescale.
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescale) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+    }
+    const float neg_m = -m_run;
     float psum = 0.f;
     bf16x8 pf[2][2];
 #pragma unroll
@@ -259,18 +293,14 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
         u32x4 pk;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = fast_exp2(sacc[h2][hh * 8 + 2 * e2] - m_use);
-          const float p1 = fast_exp2(sacc[h2][hh * 8 + 2 * e2 + 1] - m_use);
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[h2][hh * 8 + 2 * e2], c, neg_m));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[h2][hh * 8 + 2 * e2 + 1], c, neg_m));
           psum += p0 + p1;
           pk[e2] = pack_bf16x2(p0, p1);
         }
         pf[h2][hh] = __builtin_bit_cast(bf16x8, pk);
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+    l_run += psum;
 
     // O^T += V^T P^T
 #pragma unroll
