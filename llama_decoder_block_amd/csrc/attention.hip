@@ -504,6 +504,167 @@ attn_decode_kernel(AttnArgs a, int n_chunks, float* __restrict__ part_o,
   }
 }
 
+// ===========================================================================
+// decode kernel v2 (bf16, hd = 128): one wavefront per (sequence, KV group,
+// chunk of 256 slots).  The chunk is walked in sub-steps of 32 slots:
+//   * scores S = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): K rows
+//     are loaded straight into A-operand registers (lane l: slot l%16 of a
+//     16-slot block, 8 head-dim elements at (l/16)*8 + 32 s), Q^T is the B
+//     operand with the R query heads of the group as columns (other columns
+//     zero);
+//   * online softmax per query column in registers (lanes l%16 < R);
+//   * the weights go through a small per-wavefront LDS buffer to the PV lanes,
+//     which read V coalesced (16 lanes per 256-byte row) and accumulate
+//     o[r][8 elements] with fp32 FMAs.
+// Writes a partial (max, sum, o) per chunk; attn_decode_combine_kernel merges.
+// ===========================================================================
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+template <int R>
+__global__ void __launch_bounds__(256)
+attn_decode2_kernel(AttnArgs a, int n_chunks, float* __restrict__ part_o,
+                    float* __restrict__ part_ml) {
+  constexpr int HD = 128, SUB = 32, CHUNK = kDChunk;
+  __shared__ float s_p[4][SUB][R > 4 ? R : 4];   // weights [slot][query] per wavefront
+  __shared__ float s_alpha[4][R > 4 ? R : 4];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int task = blockIdx.x * 4 + w;
+  if (task >= a.B * a.nkv * n_chunks) return;
+  const int chunk = task % n_chunks;
+  const int bg = task / n_chunks;
+  const int g = bg % a.nkv, b = bg / a.nkv;
+  const int vis = min(a.positions ? a.positions[b] : 0, a.S - 1);
+  const int j0 = chunk * CHUNK;
+  if (j0 > vis) return;  // nothing visible (the combine skips this chunk)
+  const int jend = min(vis, j0 + CHUNK - 1);
+
+  const int64_t kvrow = static_cast<int64_t>(a.nkv) * HD;
+  const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
+  const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // Q^T fragments (B operand): column = query head col (< R), k = head dim
+  bf16x8_t qf[4];
+  {
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + (static_cast<int64_t>(b) * a.nq + g * R + (col < R ? col : 0)) * HD;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 t = *reinterpret_cast<const u32x4*>(qp + s * 32 + grp * 8);
+      if (col >= R) t = u32x4{0, 0, 0, 0};
+      qf[s] = __builtin_bit_cast(bf16x8_t, t);
+    }
+  }
+  const float c = a.scale * kLog2e;
+  float m_run = -INFINITY, l_run = 0.f;  // per query column (score lanes)
+  float o[R][8];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+
+  for (int js = j0; js <= jend; js += SUB) {
+    // K: 2 blocks of 16 slots x 4 head-dim steps; V: 8 slots per lane group
+    u32x4 kr[2][4], vr[8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int j = min(js + blk * 16 + col, jend);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kr[blk][s] = *reinterpret_cast<const u32x4*>(kbase + j * kvrow + s * 32 + grp * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = min(js + grp + 4 * i, jend);
+      vr[i] = *reinterpret_cast<const u32x4*>(vbase + j * kvrow + col * 8);
+    }
+    // scores: lane holds query col, slots blk*16 + grp*4 + i
+    f32x4 sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[blk][s]), qf[s], sc[blk], 0, 0, 0);
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = js + blk * 16 + grp * 4 + i;
+        if (j > jend) sc[blk][i] = -INFINITY;
+        tmax = fmaxf(tmax, sc[blk][i]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(sc[blk][i], c, -m_new));
+        psum += p;
+        if (col < R) s_p[w][blk * 16 + grp * 4 + i][col] = p;
+      }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    if (grp == 0 && col < R) s_alpha[w][col] = alpha;
+    __builtin_amdgcn_wave_barrier();
+    // PV: lane holds head-dim elements col*8 .. +7 of slots grp + 4 i
+    float al[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) al[r] = s_alpha[w][r];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][e] *= al[r];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(vr[i][q] << 16);
+        v[2 * q + 1] = __uint_as_float(vr[i][q] & 0xffff0000u);
+      }
+      const int sl = grp + 4 * i;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float p = s_p[w][sl][r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[r][e] = __builtin_fmaf(p, v[e], o[r][e]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // reduce o over the 4 lane groups, then lanes 0..15 write the partial
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = o[r][e];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      o[r][e] = v;
+    }
+  const int64_t pbase = (static_cast<int64_t>(b) * a.nq + g * R) * n_chunks + chunk;
+  if (grp == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float* po = part_o + (pbase + static_cast<int64_t>(r) * n_chunks) * HD + col * 8;
+      *reinterpret_cast<f32x4*>(po) = f32x4{o[r][0], o[r][1], o[r][2], o[r][3]};
+      *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[r][4], o[r][5], o[r][6], o[r][7]};
+    }
+  }
+  if (lane < R) {
+    part_ml[(pbase + static_cast<int64_t>(lane) * n_chunks) * 2 + 0] = m_run;
+    part_ml[(pbase + static_cast<int64_t>(lane) * n_chunks) * 2 + 1] = l_run;
+  }
+}
+
 // one wavefront per (b, h): merge the visible chunks
 template <typename T, int HD>
 __global__ void __launch_bounds__(256)
@@ -548,6 +709,21 @@ hipError_t launch_decode_t(const AttnArgs& a, void* ws, hipStream_t s) {
   float* part_ml = part_o + static_cast<int64_t>(a.B) * a.nq * nch * HD;
   const int R = a.nq / a.nkv;
   dim3 grid(a.B * a.nkv * nch);
+  if (sizeof(T) == 2 && HD == 128 && R <= 8) {
+    dim3 g2((a.B * a.nkv * nch + 3) / 4);
+    switch (R) {
+      case 1: hipLaunchKernelGGL((attn_decode2_kernel<1>), g2, dim3(256), 0, s, a, nch, part_o, part_ml); break;
+      case 2: hipLaunchKernelGGL((attn_decode2_kernel<2>), g2, dim3(256), 0, s, a, nch, part_o, part_ml); break;
+      case 4: hipLaunchKernelGGL((attn_decode2_kernel<4>), g2, dim3(256), 0, s, a, nch, part_o, part_ml); break;
+      default: hipLaunchKernelGGL((attn_decode2_kernel<8>), g2, dim3(256), 0, s, a, nch, part_o, part_ml); break;
+    }
+    hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    const int64_t waves = static_cast<int64_t>(a.B) * a.nq;
+    hipLaunchKernelGGL((attn_decode_combine_kernel<T, HD>), dim3(static_cast<unsigned>((waves + 3) / 4)),
+                       dim3(256), 0, s, a, nch, part_o, part_ml);
+    return hipGetLastError();
+  }
   switch (R) {
     case 1: hipLaunchKernelGGL((attn_decode_kernel<T, HD, 1>), grid, dim3(256), 0, s, a, nch, part_o, part_ml); break;
     case 2: hipLaunchKernelGGL((attn_decode_kernel<T, HD, 2>), grid, dim3(256), 0, s, a, nch, part_o, part_ml); break;

@@ -228,12 +228,14 @@ def test_flash_causal_future_perturbation_bitwise():
         assert not torch.equal(pert[:, t + 1:], base[:, t + 1:])
 
 
-@pytest.mark.parametrize("nq,nkv,hd", [(32, 8, 128), (8, 8, 128), (16, 2, 64)])
+@pytest.mark.parametrize("nq,nkv,hd", [(32, 8, 128), (8, 8, 128), (16, 8, 128), (32, 4, 128), (16, 2, 64)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_decode_attention(nq, nkv, hd, dtype):
-    B, S = 3, 600
+    """Visible lengths 600, 257, 1, 288 and 33: full and one-slot chunks, whole
+    and partial 32-slot steps."""
+    B, S = 5, 600
     q, k, v = attn_inputs(90, B, 1, S, nq, nkv, hd, dtype)
-    pos = torch.tensor([[599], [256], [0]], dtype=torch.int32)
+    pos = torch.tensor([[599], [256], [0], [287], [32]], dtype=torch.int32)
     out = binding.gqa_attention(dev(q), dev(k), dev(v), dev(pos))
     torch.cuda.synchronize()
     ref = oracle.gqa_attention(to64(q), to64(k), to64(v), to64(pos).astype(np.int64))
