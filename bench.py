@@ -9,15 +9,19 @@ seeded synthetic tensors already resident in device memory.  Prints one JSON
 line (rank 0).
 
 value      = prefill block-forward TFLOP/s (algorithmic FLOPs: linear layers
-             plus causal attention pairs) over the K timed steps
+             plus causal attention pairs) over the K timed steps, which run
+             back to back between two synchronizations
 roofline   = the dominant kernel (fused gate/up GEMM + SiLU product):
              algorithmic FLOPs per launch / its average launch time, measured
              with HIP events recorded on the kernel's stream inside the timed
              region
-decode     = the decode step: tokens/s, microseconds per step, and the split-K
-             attention kernel's achieved GB/s against the HBM peak
+kernels    = every timed step of the path: launches, average time, and the
+             achieved TFLOP/s (GEMMs, attention) or GB/s (norms)
+decode     = the decode step (1 GiB written between steps so that weights and
+             cache come from HBM): tokens/s, time per step, per-step kernels and
+             the split-K attention's achieved GB/s against the HBM peak
 cpu_baseline = the CPU oracle (numpy fp64) on a bounded sample of the same
-             prefill workload: the first T_s tokens of the sequence
+             prefill workload: the first --cpu-tokens tokens of the sequence
 """
 
 import argparse
@@ -41,8 +45,26 @@ HBM_PEAK_GBS = 8000.0
 
 PREFILL = "llama3_8b_gqa_prefill"
 DECODE = "llama3_8b_gqa_decode"
-DOMINANT = "gemm_mfma_gate_up_silu"
-DECODE_ATTN = "attn_decode_splitk"
+DOMINANT = "gate_up_silu/gemm_mfma_gate_up_silu"
+DECODE_ATTN = "attention/attn_decode_splitk"
+# HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes (KiB per dispatch), each scaled by the same counter's
+# reading for a plain device copy of known size (bench.py --copy-calibration:
+# FETCH_SIZE reads half the bytes the copy reads, WRITE_SIZE all of them).
+# Valid only for the GEMM sources it was measured on: reported as null once
+# their hash changes.
+TRAFFIC = {"bytes": 3111553694, "fetch_scale": 2.0, "write_scale": 1.0,
+           "sources_sha256": "e1b2b8df3d141ed6765e8365db4db0364d2726443061db2b9211d78727d219b3"}
+TRAFFIC_SOURCES = ("gemm.hip", "kernels.hpp", "common.hpp")
+
+
+def dominant_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "llama_decoder_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return TRAFFIC["bytes"] if h.hexdigest() == TRAFFIC["sources_sha256"] else None
 
 
 def log(*a):
@@ -73,26 +95,51 @@ def prepare(wl, dev):
     return step, inp
 
 
-def time_steps(step, steps, warmup):
+def time_steps(step, steps, warmup, flush=None):
+    """W untimed steps, then K timed steps with per-kernel events on.  Each step
+    is bracketed by its own pair of events; with `flush` (a callable that
+    overwrites the 256 MB last-level cache) the flush runs between steps,
+    outside every step's events, and the total is the sum of the steps."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     binding.profile_reset()
     binding.profile_enable(True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
+    for e0, e1 in ev:
+        if flush is not None:
+            flush()
+        e0.record()
         step()
-    e1.record()
+        e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     binding.profile_enable(False)
     kernels = binding.profile_collect()
-    ms = e0.elapsed_time(e1) / steps
-    return ms, wall, kernels
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    if flush is None:
+        ms = ev[0][0].elapsed_time(ev[-1][1]) / steps
+    else:
+        ms = sum(per) / steps
+    return ms, per, kernels
+
+
+def kernel_table(kernels, work):
+    """avg time per launch and the achieved rate of each timed step."""
+    rows = {}
+    for key, (n, t) in sorted(kernels.items(), key=lambda kv: -kv[1][1]):
+        avg_us = t / n * 1e3
+        step_name = key.split("/")[0]
+        flops, nbytes = work.get(step_name, (0, 0))
+        row = {"launches": n, "avg_us": round(avg_us, 2)}
+        if flops and flops / max(nbytes, 1) > 50:
+            tf = flops / (avg_us * 1e-6) / 1e12
+            row.update({"tflops": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        elif nbytes:
+            gbs = nbytes / (avg_us * 1e-6) / 1e9
+            row.update({"gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        rows[key] = row
+    return rows
 
 
 def cpu_baseline(tokens):
@@ -112,8 +159,8 @@ def cpu_baseline(tokens):
     dt = time.perf_counter() - t0
     flops = wm.prefill_flops(shape_of(wl), wl.batch, wl.seq)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"numpy fp64 block forward of the first {tokens} tokens of the T=8192 Llama-3-8B "
-                      f"prefill (same seeded inputs), {dt:.1f} s"}
+            "sample": f"numpy fp64 block forward of the first {tokens} of the {synth.workload(PREFILL).seq} "
+                      f"tokens of the Llama-3-8B prefill (same seeded inputs), one pass, {dt:.1f} s"}
 
 
 def main():
@@ -122,9 +169,12 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=50)
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) five times: the "
+                         "reference reading for scaling the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md on sharding); "
@@ -134,6 +184,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = "cuda:0"
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 5 x {src.numel() * 4} bytes read and written")
+        return
     binding.lib()
 
     # ---------------- prefill -----------------
@@ -141,18 +199,21 @@ def main():
     log(f"[bench] preparing {PREFILL}")
     step, _ = prepare(wl, dev)
     log(f"[bench] prefill: warmup {args.warmup}, timing {args.steps} steps")
-    ms, wall, kernels = time_steps(step, args.steps, args.warmup)
+    ms, per, kernels = time_steps(step, args.steps, args.warmup)
     sh = shape_of(wl)
     flops = wm.prefill_flops(sh, wl.batch, wl.seq)
     tflops = flops / (ms * 1e-3) / 1e12
     tok_s = wl.batch * wl.seq / (ms * 1e-3)
+    work = wm.step_work(sh, wl.batch, wl.seq)
+    table = kernel_table(kernels, work)
     n_dom, ms_dom = kernels.get(DOMINANT, (0, 0.0))
-    dom_flops = wm.gemm_flops(wl.batch * wl.seq, 2 * wl.d_ff, wl.d_model)
+    dom_flops = work["gate_up_silu"][0]
     dom_avg_ms = ms_dom / max(n_dom, 1)
     dom_tflops = dom_flops / (dom_avg_ms * 1e-3) / 1e12 if n_dom else 0.0
-    log(f"[bench] prefill {ms:.3f} ms/step, {tflops:.1f} TFLOP/s, {tok_s/1e6:.3f} M tok/s")
-    for k, (n, t) in sorted(kernels.items(), key=lambda kv: -kv[1][1]):
-        log(f"[bench]   {k:28s} launches={n:4d} avg={t / n * 1e3:9.1f} us  share={t / (ms * args.steps):6.1%}")
+    log(f"[bench] prefill {ms:.3f} ms/step (median {per[len(per) // 2]:.3f}, min {per[0]:.3f}), "
+        f"{tflops:.1f} TFLOP/s, {tok_s / 1e6:.3f} M tok/s")
+    for k, row in table.items():
+        log(f"[bench]   {k:40s} {row}")
     del step
     torch.cuda.empty_cache()
 
@@ -162,31 +223,40 @@ def main():
         wd = synth.workload(DECODE)
         log(f"[bench] preparing {DECODE}")
         dstep, _ = prepare(wd, dev)
-        dms, _, dk = time_steps(dstep, args.decode_steps, args.warmup)
+        # 1 GiB overwritten between steps so that neither weights nor cache are
+        # served from the 256 MB last-level cache
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dms, dper, dk = time_steps(dstep, args.decode_steps, args.warmup, flush=scratch.zero_)
+        del scratch
         shd = shape_of(wd)
         attend = wd.decode_pos + 1
+        dwork = wm.step_work(shd, wd.batch, 1, attend_len=attend)
+        dtable = kernel_table(dk, dwork)
         n_at, ms_at = dk.get(DECODE_ATTN, (0, 0.0))
-        # attention: the split-K kernel plus its combine pass are timed together
-        at_avg = ms_at / max(n_at, 1)
-        at_bytes = wm.decode_attention_bytes(shd, wd.batch, attend)
+        at_avg = ms_at / max(n_at, 1)  # split-K pass and its combine pass together
+        at_bytes = dwork["attention"][1]
         at_gbs = at_bytes / (at_avg * 1e-3) / 1e9 if n_at else 0.0
         step_bytes = at_bytes + wm.decode_weight_bytes(shd)
         decode = {
             "workload": f"{DECODE}: B={wd.batch} x 1 token at position {wd.decode_pos}, KV cache "
-                        f"[{wd.batch},{wd.kv_cap},{wd.n_kv},{wd.head_dim}] bf16",
+                        f"[{wd.batch},{wd.kv_cap},{wd.n_kv},{wd.head_dim}] bf16, last-level cache flushed "
+                        f"between steps",
             "ms_per_step": round(dms, 4),
+            "ms_median": round(dper[len(dper) // 2], 4),
+            "ms_min": round(dper[0], 4),
             "tokens_per_s": round(wd.batch / (dms * 1e-3), 1),
             "step_tflops": round(wm.decode_flops(shd, wd.batch, attend) / (dms * 1e-3) / 1e12, 3),
             "step_gbs": round(step_bytes / (dms * 1e-3) / 1e9, 1),
             "step_hbm_frac": round(step_bytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "attention": {"kernel": DECODE_ATTN, "avg_us": round(at_avg * 1e3, 2),
+            "attention": {"kernel": DECODE_ATTN, "bound": "hbm", "avg_us": round(at_avg * 1e3, 2),
                           "bytes": at_bytes, "achieved": round(at_gbs, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(at_gbs / HBM_PEAK_GBS, 4)},
-            "kernels_us": {k: round(t / n * 1e3, 2) for k, (n, t) in dk.items()},
+            "kernels": dtable,
         }
-        log(f"[bench] decode {dms * 1e3:.1f} us/step, attention {at_avg * 1e3:.1f} us = {at_gbs:.0f} GB/s")
-        for k, (n, t) in sorted(dk.items(), key=lambda kv: -kv[1][1]):
-            log(f"[bench]   {k:28s} launches={n:4d} avg={t / n * 1e3:9.1f} us")
+        log(f"[bench] decode {dms * 1e3:.1f} us/step (median {dper[len(dper) // 2] * 1e3:.1f}, "
+            f"min {dper[0] * 1e3:.1f}), attention {at_avg * 1e3:.1f} us = {at_gbs:.0f} GB/s")
+        for k, row in dtable.items():
+            log(f"[bench]   {k:40s} {row}")
         del dstep
         torch.cuda.empty_cache()
 
@@ -194,6 +264,7 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")
         cpu = cpu_baseline(args.cpu_tokens)
+        log(f"[bench] cpu baseline: {cpu}")
 
     out = {
         "metric": "block fwd TFLOP/s + tokens/s (prefill & decode), % of MFMA/HBM roofline",
@@ -203,6 +274,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_median": round(per[len(per) // 2], 4),
+        "ms_min": round(per[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -215,9 +288,9 @@ def main():
         "prefill_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"kernel": DOMINANT, "bound": "mfma", "achieved": round(dom_tflops, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(dom_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": dominant_traffic(),
                      "flops_per_launch": dom_flops, "avg_us": round(dom_avg_ms * 1e3, 2)},
-        "kernels_us": {k: round(t / n * 1e3, 2) for k, (n, t) in kernels.items()},
+        "kernels": table,
         "decode": decode,
         "cpu_baseline": cpu,
     }

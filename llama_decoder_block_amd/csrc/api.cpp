@@ -72,10 +72,12 @@ hipEvent_t take_event() {
   return e;
 }
 
-// Runs `launch` (which enqueues exactly the kernels of one named step) and,
-// when timing is on, brackets it with events on the same stream.
+// Runs `launch` (which enqueues exactly the kernels of one step of the path)
+// and, when timing is on, brackets it with events on the same stream.  The
+// record is keyed "step/kernel" (or just "step" when the launcher names no
+// kernel variant, or names the step itself).
 template <class F>
-hipError_t timed(const char* fallback_name, hipStream_t s, F&& launch) {
+hipError_t timed(const char* step, hipStream_t s, F&& launch) {
   if (!g_prof_on) {
     const char* name = nullptr;
     return launch(&name);
@@ -85,8 +87,11 @@ hipError_t timed(const char* fallback_name, hipStream_t s, F&& launch) {
   const char* name = nullptr;
   hipError_t err = launch(&name);
   if (e1) (void)hipEventRecord(e1, s);
-  if (e0 && e1)
-    g_pending.push_back({name ? name : fallback_name, e0, e1});
+  if (e0 && e1) {
+    std::string key(step);
+    if (name && key != name) key += std::string("/") + name;
+    g_pending.push_back({key, e0, e1});
+  }
   return err;
 }
 
@@ -257,7 +262,7 @@ hipError_t run_ffn(const void* x, const void* w_gate, const void* w_up, const vo
   gu.ptr[0] = w_gate; gu.ptr[1] = w_up; gu.start[0] = 0; gu.start[1] = dff; gu.start[2] = 2 * dff; gu.nseg = 2;
   lb::GemmEpi e1{};
   e1.kind = lb::EpiKind::Silu; e1.out_dt = wdt; e1.out = mact; e1.ldo = dff;
-  hipError_t e = timed("gemm_gate_up", s, [&](const char** name) {
+  hipError_t e = timed("gate_up_silu", s, [&](const char** name) {
     return lb::launch_gemm(wdt, x, n, d, gu, dff, true, e1, gws, gws_bytes, s, name);
   });
   if (e != hipSuccess) return e;
@@ -269,7 +274,7 @@ hipError_t run_ffn(const void* x, const void* w_gate, const void* w_up, const vo
   } else {
     e2.kind = lb::EpiKind::Store; e2.out_dt = rdt; e2.out = out; e2.ldo = d;
   }
-  return timed("gemm_down", s, [&](const char** name) {
+  return timed("down_resid", s, [&](const char** name) {
     return lb::launch_gemm(wdt, mact, n, dff, dn, d, false, e2, gws, gws_bytes, s, name);
   });
 }
@@ -408,7 +413,7 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
   hipError_t e;
 
   // a1: attention pre-norm
-  e = timed("rmsnorm", s, [&](const char** name) {
+  e = timed("attn_norm", s, [&](const char** name) {
     *name = "rmsnorm";
     return lb::launch_rmsnorm(x, nullptr, w->attn_norm, a_buf, nullptr, M, d, feps, wdt, rdt, s);
   });
@@ -425,7 +430,7 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
     ep.q = q_buf; ep.k = k_buf; ep.v = v_buf; ep.positions = positions;
     ep.nq_hd = nq * hd; ep.nkv_hd = nkv * hd; ep.hd = hd; ep.seq_len = T; ep.kv_cap = kv_cap;
     ep.rope = &rope;
-    e = timed("gemm_qkv_rope", s, [&](const char** name) {
+    e = timed("qkv_rope", s, [&](const char** name) {
       return lb::launch_gemm(wdt, a_buf, M, d, wqkv, (nq + 2 * nkv) * hd, false, ep, gemm_ws, p.gemm, s, name);
     });
     if (e != hipSuccess) return hip_fail(e, "llama_block_forward: qkv projection");
@@ -450,14 +455,14 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
     wo.ptr[0] = w->wo; wo.start[0] = 0; wo.start[1] = d; wo.nseg = 1;
     lb::GemmEpi ep{};
     ep.kind = lb::EpiKind::Resid; ep.out_dt = rdt; ep.out = h_buf; ep.resid = x; ep.ldo = d;
-    e = timed("gemm_o_resid", s, [&](const char** name) {
+    e = timed("o_resid", s, [&](const char** name) {
       return lb::launch_gemm(wdt, o_buf, M, nq * hd, wo, d, false, ep, gemm_ws, p.gemm, s, name);
     });
     if (e != hipSuccess) return hip_fail(e, "llama_block_forward: o projection");
   }
 
   // a8: FFN pre-norm (f reuses the a buffer)
-  e = timed("rmsnorm", s, [&](const char** name) {
+  e = timed("ffn_norm", s, [&](const char** name) {
     *name = "rmsnorm";
     return lb::launch_rmsnorm(h_buf, nullptr, w->ffn_norm, a_buf, nullptr, M, d, feps, wdt, rdt, s);
   });

@@ -87,3 +87,35 @@ def decode_weight_bytes(s, elem_bytes=2):
 
 def gemm_flops(m, n, k):
     return 2 * m * n * k
+
+
+def step_work(s, batch, seq, attend_len=None, wbytes=2, rbytes=4):
+    """Algorithmic FLOPs and HBM bytes of each step of one block forward.
+
+    Returns {step: (flops, bytes)} keyed like the library's timing records
+    (attn_norm, qkv_rope, attention, o_resid, ffn_norm, gate_up_silu,
+    down_resid).  `attend_len` is None for a prefill without a cache (causal
+    pairs within the sequence) and the number of visible cache slots for a
+    one-token decode.  Bytes: every weight, input and output read or written
+    once; for decode attention only the K/V slots are counted (the query and
+    output are 1/4000 of it).  `wbytes` / `rbytes` are the element sizes of
+    the GEMM operands and of the residual stream.
+    """
+    m = batch * seq
+    d, hd = s.d_model, s.head_dim
+    nqkv = (s.n_q + 2 * s.n_kv) * hd
+    nqo = s.n_q * hd
+    out = {}
+    norm_bytes = m * d * (rbytes + wbytes) + d * wbytes
+    out["attn_norm"] = (0, norm_bytes)
+    out["qkv_rope"] = (gemm_flops(m, nqkv, d), (nqkv * d + m * d + m * nqkv) * wbytes)
+    if attend_len is None:
+        out["attention"] = (prefill_attention_flops(s, batch, seq), m * (nqkv + nqo) * wbytes)
+    else:
+        out["attention"] = (decode_attention_flops(s, batch, attend_len),
+                            decode_attention_bytes(s, batch, attend_len, wbytes))
+    out["o_resid"] = (gemm_flops(m, d, nqo), (d * nqo + m * nqo) * wbytes + 2 * m * d * rbytes)
+    out["ffn_norm"] = (0, norm_bytes)
+    out["gate_up_silu"] = (gemm_flops(m, 2 * s.d_ff, d), (2 * s.d_ff * d + m * d + m * s.d_ff) * wbytes)
+    out["down_resid"] = (gemm_flops(m, d, s.d_ff), (d * s.d_ff + m * s.d_ff) * wbytes + 2 * m * d * rbytes)
+    return out

@@ -42,3 +42,14 @@ def test_kv_cache_bytes():
     assert 32 * wm.kv_bytes_per_token(wm.Shape(4096, 32, 32, 128, 14336)) == 524_288
     # 8192-token context over 32 layers is 1 GiB
     assert 32 * 8192 * wm.kv_bytes_per_token(L3_8B) == 1 << 30
+
+
+def test_step_work_sums_to_block_totals():
+    pre = wm.step_work(L3_8B, 1, 8192)
+    assert sum(f for f, _ in pre.values()) == wm.prefill_flops(L3_8B, 1, 8192)
+    dec = wm.step_work(L3_8B, 64, 1, attend_len=4097)
+    assert sum(f for f, _ in dec.values()) == wm.decode_flops(L3_8B, 64, 4097)
+    assert dec["attention"][1] == 1_074_003_968
+    # decode: the weights dominate the GEMM steps' bytes (activations add ~2%)
+    wbytes = sum(dec[k][1] for k in ("qkv_rope", "o_resid", "gate_up_silu", "down_resid"))
+    assert wm.decode_weight_bytes(L3_8B) < wbytes < 1.03 * wm.decode_weight_bytes(L3_8B)
