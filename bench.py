@@ -17,7 +17,7 @@ roofline   = the dominant kernel (fused gate/up GEMM + SiLU product):
              region
 kernels    = every timed step of the path: launches, average time, and the
              achieved TFLOP/s (GEMMs, attention) or GB/s (norms)
-decode     = the decode step (1 GiB written between steps so that weights and
+decode     = the decode step (1 GiB read between steps so that weights and
              cache come from HBM): tokens/s, time per step, per-step kernels and
              the split-K attention's achieved GB/s against the HBM peak
 cpu_baseline = the CPU oracle (numpy fp64) on a bounded sample of the same
@@ -46,7 +46,7 @@ HBM_PEAK_GBS = 8000.0
 PREFILL = "llama3_8b_gqa_prefill"
 DECODE = "llama3_8b_gqa_decode"
 DOMINANT = "gate_up_silu/gemm_mfma_gate_up_silu"
-DECODE_ATTN = "attention/attn_decode_splitk"
+DECODE_ATTN = "attention/attn_decode_wg"
 # HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE passes (KiB per dispatch), each scaled by the same counter's
 # reading for a plain device copy of known size (bench.py --copy-calibration:
@@ -223,10 +223,12 @@ def main():
         wd = synth.workload(DECODE)
         log(f"[bench] preparing {DECODE}")
         dstep, _ = prepare(wd, dev)
-        # 1 GiB overwritten between steps so that neither weights nor cache are
-        # served from the 256 MB last-level cache
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dms, dper, dk = time_steps(dstep, args.decode_steps, args.warmup, flush=scratch.zero_)
+        # 1 GiB read between steps so that neither weights nor cache are served
+        # from the 256 MB last-level cache.  A read, not a write: written lines
+        # would sit dirty in the cache and their write-back would be charged to
+        # the next step.
+        scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        dms, dper, dk = time_steps(dstep, args.decode_steps, args.warmup, flush=lambda: scratch.sum())
         del scratch
         shd = shape_of(wd)
         attend = wd.decode_pos + 1
@@ -240,7 +242,7 @@ def main():
         decode = {
             "workload": f"{DECODE}: B={wd.batch} x 1 token at position {wd.decode_pos}, KV cache "
                         f"[{wd.batch},{wd.kv_cap},{wd.n_kv},{wd.head_dim}] bf16, last-level cache flushed "
-                        f"between steps",
+                        f"(1 GiB read) between steps",
             "ms_per_step": round(dms, 4),
             "ms_median": round(dper[len(dper) // 2], 4),
             "ms_min": round(dper[0], 4),

@@ -16,13 +16,20 @@
 //   O^T = V^T P^T.  V is written to LDS transposed for that product.
 //   Accumulators, running max and sum are fp32; P is rounded to bf16 for the
 //   MFMA.  Only tiles at or below each workgroup's last visible slot are read.
-// attn_decode_kernel (one query token per sequence): split-K over the key
-//   slots.  One workgroup per (sequence, KV group, chunk of 256 slots) streams
-//   its chunk of K and V once (16-byte loads, all issued up front) for the R
-//   query heads of the group and writes a partial (max, sum, output);
-//   attn_decode_combine_kernel merges the chunks.
+// attn_decode3_kernel (bf16, hd = 128, one query token per sequence): one
+//   workgroup per (sequence, KV group) whose wavefronts split the visible
+//   slots; each streams its K/V rows once for the R query heads of the group
+//   (scores on v_mfma_f32_16x16x32_bf16 with K rows loaded straight into
+//   A-operand registers), and the workgroup merges the partial softmax
+//   states in LDS.  attn_decode2_kernel + attn_decode_combine_kernel do the
+//   same with chunks spread over workgroups and merged through HBM when there
+//   are too few (sequence, KV group) pairs to fill the chip.
+// attn_decode_kernel (fp32 or hd = 64): split-K over 256-slot chunks, one
+//   workgroup per (sequence, KV group, chunk), merged by the combine kernel.
 // attn_valu_kernel: generic fp32-accumulating kernel (one wavefront per query
 //   row, online softmax over 64-slot chunks) for fp32 and other shapes.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -55,7 +62,7 @@ attn_valu_kernel(AttnArgs a) {
   __syncthreads();
   if (!active) return;
   const int g = h / (a.nq / a.nkv);
-  const int vis = a.positions ? a.positions[bt] : t;
+  const int vis = min(a.positions ? a.positions[bt] : t, a.S - 1);
   const T* kb = static_cast<const T*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * a.hd;
   const T* vb = static_cast<const T*>(a.v) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * a.hd;
   const int64_t kstride = static_cast<int64_t>(a.nkv) * a.hd;
@@ -342,7 +349,7 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
 // ===========================================================================
 // split-K decode kernel + combine
 // ===========================================================================
-constexpr int kDChunk = 256;  // key slots per workgroup
+constexpr int kDChunk = 256;  // key slots per chunk of attn_decode_kernel (and the minimum split-K chunk)
 
 template <typename T> struct VecN;            // 16-byte vector of T
 template <> struct VecN<bf16_t> { static constexpr int N = 8; };
@@ -382,7 +389,7 @@ attn_decode_kernel(AttnArgs a, int n_chunks, float* __restrict__ part_o,
   const int chunk = blockIdx.x % n_chunks;
   const int bg = blockIdx.x / n_chunks;
   const int g = bg % a.nkv, b = bg / a.nkv;
-  const int vis = a.positions ? a.positions[b] : 0;  // q_len == 1
+  const int vis = min(a.positions ? a.positions[b] : 0, a.S - 1);  // q_len == 1
   const int j0 = chunk * kDChunk;
   if (j0 > vis) return;  // nothing visible in this chunk (combine skips it)
   const int jn = min(kDChunk, vis - j0 + 1);
@@ -520,13 +527,134 @@ attn_decode_kernel(AttnArgs a, int n_chunks, float* __restrict__ part_o,
 // ===========================================================================
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
+constexpr int kDSub = 32;  // slots per step of the decode wavefront
+
+// Sum / max over the four 16-lane rows of a wavefront (lanes l, l^16, l^32,
+// l^48): v_permlane32_swap then v_permlane16_swap exchange the rows on the
+// VALU (no LDS round trip).
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// K/V registers of one 32-slot step: K as two 16-slot MFMA A blocks x 4
+// head-dim steps, V as 8 slots per lane group (16 lanes per 256-byte row).
+struct DecRegs {
+  u32x4 k[2][4];
+  u32x4 v[8];
+};
+
+__device__ __forceinline__ void dec_load(DecRegs& r, const bf16_t* kbase, const bf16_t* vbase,
+                                         int64_t kvrow, int js, int jend, int col, int grp) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int j = min(js + blk * 16 + col, jend);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) r.k[blk][s] = *reinterpret_cast<const u32x4*>(kbase + j * kvrow + s * 32 + grp * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = min(js + grp + 4 * i, jend);
+    r.v[i] = *reinterpret_cast<const u32x4*>(vbase + j * kvrow + col * 8);
+  }
+}
+
+template <int R>
+struct DecState {
+  static constexpr int RP = R > 4 ? R : 4;
+  float m_run, l_run;  // per query column (score lanes)
+  float o[R][8];       // head-dim elements col*8 .. +7, summed over lane groups at the end
+
+  __device__ __forceinline__ void init() {
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+  }
+
+  // one 32-slot step: scores on the matrix cores, online softmax, PV on the VALU
+  __device__ __forceinline__ void step(const DecRegs& kv, const bf16x8_t (&qf)[4], float c, int js, int jend,
+                                       int col, int grp, float (*s_p)[RP], float* s_alpha) {
+    f32x4 sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv.k[blk][s]), qf[s], sc[blk],
+                                                          0, 0, 0);
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = js + blk * 16 + grp * 4 + i;
+        if (j > jend) sc[blk][i] = -INFINITY;
+        tmax = fmaxf(tmax, sc[blk][i]);
+      }
+    tmax = rows_max(tmax) * c;
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(sc[blk][i], c, -m_new));
+        psum += p;
+        if (col < R) s_p[blk * 16 + grp * 4 + i][col] = p;
+      }
+    l_run = l_run * alpha + rows_sum(psum);
+    if (grp == 0 && col < R) s_alpha[col] = alpha;
+    __builtin_amdgcn_wave_barrier();
+    float al[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) al[r] = s_alpha[r];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][e] *= al[r];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(kv.v[i][q] << 16);
+        v[2 * q + 1] = __uint_as_float(kv.v[i][q] & 0xffff0000u);
+      }
+      const int sl = grp + 4 * i;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float p = s_p[sl][r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[r][e] = __builtin_fmaf(p, v[e], o[r][e]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+};
+
 template <int R>
 __global__ void __launch_bounds__(256)
-attn_decode2_kernel(AttnArgs a, int n_chunks, float* __restrict__ part_o,
+attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__ part_o,
                     float* __restrict__ part_ml) {
-  constexpr int HD = 128, SUB = 32, CHUNK = kDChunk;
-  __shared__ float s_p[4][SUB][R > 4 ? R : 4];   // weights [slot][query] per wavefront
-  __shared__ float s_alpha[4][R > 4 ? R : 4];
+  constexpr int HD = 128, SUB = kDSub;
+  const int CHUNK = chunk_len;
+  using St = DecState<R>;
+  __shared__ float s_p[4][SUB][St::RP];   // weights [slot][query] per wavefront
+  __shared__ float s_alpha[4][St::RP];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int task = blockIdx.x * 4 + w;
   if (task >= a.B * a.nkv * n_chunks) return;
@@ -555,89 +683,12 @@ attn_decode2_kernel(AttnArgs a, int n_chunks, float* __restrict__ part_o,
     }
   }
   const float c = a.scale * kLog2e;
-  float m_run = -INFINITY, l_run = 0.f;  // per query column (score lanes)
-  float o[R][8];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
-
+  St st;
+  st.init();
   for (int js = j0; js <= jend; js += SUB) {
-    // K: 2 blocks of 16 slots x 4 head-dim steps; V: 8 slots per lane group
-    u32x4 kr[2][4], vr[8];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int j = min(js + blk * 16 + col, jend);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kr[blk][s] = *reinterpret_cast<const u32x4*>(kbase + j * kvrow + s * 32 + grp * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = min(js + grp + 4 * i, jend);
-      vr[i] = *reinterpret_cast<const u32x4*>(vbase + j * kvrow + col * 8);
-    }
-    // scores: lane holds query col, slots blk*16 + grp*4 + i
-    f32x4 sc[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[blk][s]), qf[s], sc[blk], 0, 0, 0);
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = js + blk * 16 + grp * 4 + i;
-        if (j > jend) sc[blk][i] = -INFINITY;
-        tmax = fmaxf(tmax, sc[blk][i]);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(sc[blk][i], c, -m_new));
-        psum += p;
-        if (col < R) s_p[w][blk * 16 + grp * 4 + i][col] = p;
-      }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    if (grp == 0 && col < R) s_alpha[w][col] = alpha;
-    __builtin_amdgcn_wave_barrier();
-    // PV: lane holds head-dim elements col*8 .. +7 of slots grp + 4 i
-    float al[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) al[r] = s_alpha[w][r];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[r][e] *= al[r];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] = __uint_as_float(vr[i][q] << 16);
-        v[2 * q + 1] = __uint_as_float(vr[i][q] & 0xffff0000u);
-      }
-      const int sl = grp + 4 * i;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float p = s_p[w][sl][r];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[r][e] = __builtin_fmaf(p, v[e], o[r][e]);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
+    DecRegs rr;
+    dec_load(rr, kbase, vbase, kvrow, js, jend, col, grp);
+    st.step(rr, qf, c, js, jend, col, grp, s_p[w], s_alpha[w]);
   }
 
   // reduce o over the 4 lane groups, then lanes 0..15 write the partial
@@ -645,85 +696,262 @@ attn_decode2_kernel(AttnArgs a, int n_chunks, float* __restrict__ part_o,
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float v = o[r][e];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      o[r][e] = v;
+      st.o[r][e] = rows_sum(st.o[r][e]);
     }
   const int64_t pbase = (static_cast<int64_t>(b) * a.nq + g * R) * n_chunks + chunk;
   if (grp == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float* po = part_o + (pbase + static_cast<int64_t>(r) * n_chunks) * HD + col * 8;
-      *reinterpret_cast<f32x4*>(po) = f32x4{o[r][0], o[r][1], o[r][2], o[r][3]};
-      *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[r][4], o[r][5], o[r][6], o[r][7]};
+      *reinterpret_cast<f32x4*>(po) = f32x4{st.o[r][0], st.o[r][1], st.o[r][2], st.o[r][3]};
+      *reinterpret_cast<f32x4*>(po + 4) = f32x4{st.o[r][4], st.o[r][5], st.o[r][6], st.o[r][7]};
     }
   }
   if (lane < R) {
-    part_ml[(pbase + static_cast<int64_t>(lane) * n_chunks) * 2 + 0] = m_run;
-    part_ml[(pbase + static_cast<int64_t>(lane) * n_chunks) * 2 + 1] = l_run;
+    part_ml[(pbase + static_cast<int64_t>(lane) * n_chunks) * 2 + 0] = st.m_run;
+    part_ml[(pbase + static_cast<int64_t>(lane) * n_chunks) * 2 + 1] = st.l_run;
   }
 }
 
-// one wavefront per (b, h): merge the visible chunks
+// ===========================================================================
+// decode kernel, workgroup-combined (bf16, hd = 128): one workgroup of NW
+// wavefronts per (sequence, KV head).  Wavefront w walks slots
+// [w*per, (w+1)*per) of the visible range exactly as attn_decode2_kernel does
+// (MFMA scores, online softmax, VALU PV), leaves its (max, sum, o) in LDS, and
+// after one barrier the workgroup merges the NW partials and writes the R
+// output rows.  NW is chosen on the host so that all wavefronts of the launch
+// are resident at once; nothing goes through HBM but K, V, q and the output.
+// ===========================================================================
+// At most 16 wavefronts per workgroup (8 for R = 8, whose accumulators need
+// more than the 128 registers a 16-wavefront workgroup leaves per lane).
+template <int R>
+__global__ void __launch_bounds__(R >= 8 ? 512 : 1024)
+attn_decode3_kernel(AttnArgs a) {
+  constexpr int HD = 128, SUB = kDSub;
+  using St = DecState<R>;
+  constexpr int RP = St::RP;
+  extern __shared__ float dsm[];
+  const int nw = blockDim.x >> 6;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float(*s_p)[SUB][RP] = reinterpret_cast<float(*)[SUB][RP]>(dsm);
+  float* s_ml = dsm + nw * SUB * RP;  // [nw][R][2]
+  float* s_o = s_ml + nw * R * 2;     // [nw][R][HD]
+  const int g = blockIdx.x % a.nkv, b = blockIdx.x / a.nkv;
+  const int vis = min(a.positions ? a.positions[b] : 0, a.S - 1);
+  const int per = ((vis + nw) / nw + SUB - 1) / SUB * SUB;  // slots per wavefront, whole steps
+  const int j0 = w * per;
+  const int jend = min(vis, j0 + per - 1);
+
+  const int64_t kvrow = static_cast<int64_t>(a.nkv) * HD;
+  const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
+  const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
+  const int col = lane & 15, grp = lane >> 4;
+  bf16x8_t qf[4];
+  {
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + (static_cast<int64_t>(b) * a.nq + g * R + (col < R ? col : 0)) * HD;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 t = *reinterpret_cast<const u32x4*>(qp + s * 32 + grp * 8);
+      if (col >= R) t = u32x4{0, 0, 0, 0};
+      qf[s] = __builtin_bit_cast(bf16x8_t, t);
+    }
+  }
+  const float c = a.scale * kLog2e;
+  St st;
+  st.init();
+  float* my_alpha = s_ml + w * R * 2;  // scratch for the step's rescale factors (before the final write)
+  for (int js = j0; js <= jend; js += SUB) {
+    DecRegs rr;
+    dec_load(rr, kbase, vbase, kvrow, js, jend, col, grp);
+    st.step(rr, qf, c, js, jend, col, grp, s_p[w], my_alpha);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.o[r][e] = rows_sum(st.o[r][e]);
+  if (grp == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float* po = s_o + (w * R + r) * HD + col * 8;
+      *reinterpret_cast<f32x4*>(po) = f32x4{st.o[r][0], st.o[r][1], st.o[r][2], st.o[r][3]};
+      *reinterpret_cast<f32x4*>(po + 4) = f32x4{st.o[r][4], st.o[r][5], st.o[r][6], st.o[r][7]};
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < R) {
+    s_ml[(w * R + lane) * 2 + 0] = st.m_run;
+    s_ml[(w * R + lane) * 2 + 1] = st.l_run;
+  }
+  __syncthreads();
+  bf16_t* out = static_cast<bf16_t*>(a.out) + (static_cast<int64_t>(b) * a.nq + g * R) * HD;
+  for (int idx = threadIdx.x; idx < R * HD; idx += blockDim.x) {
+    const int r = idx / HD, d = idx - r * HD;
+    float mx = -INFINITY;
+    for (int w2 = 0; w2 < nw; ++w2) mx = fmaxf(mx, s_ml[(w2 * R + r) * 2]);
+    float l = 0.f, o = 0.f;
+    for (int w2 = 0; w2 < nw; ++w2) {
+      const float f = fast_exp2(s_ml[(w2 * R + r) * 2] - mx);
+      l += s_ml[(w2 * R + r) * 2 + 1] * f;
+      o += s_o[(w2 * R + r) * HD + d] * f;
+    }
+    out[idx] = f32_to_bf16(o / l);
+  }
+}
+
+size_t decode3_lds_bytes(int R, int nw) {
+  const int rp = R > 4 ? R : 4;
+  return static_cast<size_t>(nw) * (kDSub * rp + R * 2 + R * 128) * sizeof(float);
+}
+
+// one wavefront per (b, h): merge the visible chunks.  The chunk maxima and
+// sums are reduced across lanes; each lane then owns HD/64 consecutive output
+// elements and accumulates the chunks with all their loads independent.
 template <typename T, int HD>
 __global__ void __launch_bounds__(256)
-attn_decode_combine_kernel(AttnArgs a, int n_chunks, const float* __restrict__ part_o,
+attn_decode_combine_kernel(AttnArgs a, int n_chunks, int chunk_len, const float* __restrict__ part_o,
                            const float* __restrict__ part_ml) {
+  constexpr int E = HD / 64 > 0 ? HD / 64 : 1;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * 4 + w;
   if (bh >= static_cast<int64_t>(a.B) * a.nq) return;
   const int b = static_cast<int>(bh / a.nq);
-  const int vis = a.positions ? a.positions[b] : 0;
-  const int nvalid = min(n_chunks, vis / kDChunk + 1);
+  const int vis = min(a.positions ? a.positions[b] : 0, a.S - 1);
+  const int nvalid = vis < 0 ? 0 : min(n_chunks, vis / chunk_len + 1);
   const float* ml = part_ml + bh * n_chunks * 2;
   float mx = -INFINITY;
-  for (int ch = 0; ch < nvalid; ++ch) mx = fmaxf(mx, ml[2 * ch]);
+  for (int ch = lane; ch < nvalid; ch += 64) mx = fmaxf(mx, ml[2 * ch]);
+  mx = wave_max(mx);
   float lsum = 0.f;
-  float o[HD / 64 > 0 ? HD / 64 : 1] = {};
+  for (int ch = lane; ch < nvalid; ch += 64) lsum += ml[2 * ch + 1] * fast_exp2(ml[2 * ch] - mx);
+  lsum = wave_sum(lsum);
+  float o[E] = {};
+  const float* po = part_o + bh * n_chunks * HD + lane * E;
+#pragma unroll 8
   for (int ch = 0; ch < nvalid; ++ch) {
     const float f = fast_exp2(ml[2 * ch] - mx);
-    lsum += ml[2 * ch + 1] * f;
-    const float* po = part_o + (bh * n_chunks + ch) * HD;
 #pragma unroll
-    for (int i = 0; i < (HD + 63) / 64; ++i) {
-      const int d = lane + 64 * i;
-      if (d < HD) o[i] += po[d] * f;
-    }
+    for (int i = 0; i < E; ++i) o[i] += po[ch * HD + i] * f;
   }
   const float inv = 1.f / lsum;
-  T* out = static_cast<T*>(a.out) + bh * HD;
+  T* out = static_cast<T*>(a.out) + bh * HD + lane * E;
+  if (lane * E < HD) {
 #pragma unroll
-  for (int i = 0; i < (HD + 63) / 64; ++i) {
-    const int d = lane + 64 * i;
-    if (d < HD) st(out + d, o[i] * inv);
+    for (int i = 0; i < E; ++i) st(out + i, o[i] * inv);
   }
 }
 
 int decode_chunks(int S) { return (S + kDChunk - 1) / kDChunk; }
 
+int device_cus() {
+  static thread_local int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached_dev = dev;
+    cached_cus = n;
+  }
+  return cached_cus;
+}
+
+constexpr size_t kD3MaxLds = 64 * 1024;
+
+template <int R>
+constexpr int d3_max_waves() { return R >= 8 ? 8 : 16; }
+
+// Workgroups of attn_decode3_kernel<R> with nw wavefronts that one CU holds
+// at once (register, LDS and wave-slot limits), cached per device.
+template <int R>
+int d3_blocks_per_cu(int nw) {
+  static thread_local int cached_dev = -1;
+  static thread_local int cache[17];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev != cached_dev) {
+    for (int& c : cache) c = -1;
+    cached_dev = dev;
+  }
+  if (cache[nw] < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_decode3_kernel<R>, 64 * nw,
+                                                     decode3_lds_bytes(R, nw)) != hipSuccess)
+      n = 0;
+    cache[nw] = n;
+  }
+  return cache[nw];
+}
+
+// Wavefronts in flight for the bf16 decode kernels: about 6 per CU.  On
+// MI355X the K/V stream of the B=64, 4097-slot workload measured 5.75 TB/s
+// with 6 wavefronts per CU (1536 streams), against 5.2-5.5 TB/s with 4, 8, 10
+// or 16: more concurrent streams than that cost HBM page locality, fewer
+// leave bandwidth idle.
+constexpr int kDecWavesPerCu = 6;
+
+// Wavefronts per (sequence, KV head) workgroup of attn_decode3_kernel: close
+// to the target count, all workgroups resident in one round, within LDS.
+template <int R>
+int d3_pick_waves(int64_t pairs, int64_t target) {
+  const int cus = device_cus();
+  int nw = static_cast<int>(std::min<int64_t>(d3_max_waves<R>(), std::max<int64_t>(1, (target + pairs / 2) / pairs)));
+  while (nw > 1 && (decode3_lds_bytes(R, nw) > kD3MaxLds ||
+                    pairs > static_cast<int64_t>(d3_blocks_per_cu<R>(nw)) * cus))
+    --nw;
+  return nw;
+}
+
+template <int R>
+hipError_t launch_decode_bf16(const AttnArgs& a, void* ws, hipStream_t s, const char** kernel_name) {
+  constexpr int HD = 128;
+  const int64_t pairs = static_cast<int64_t>(a.B) * a.nkv;
+  const int64_t target = static_cast<int64_t>(device_cus()) * kDecWavesPerCu;
+  const int nw = d3_pick_waves<R>(pairs, target);
+  if (pairs * nw * 2 >= target) {
+    // one workgroup per (sequence, KV head) reaches at least half the target
+    if (kernel_name) *kernel_name = "attn_decode_wg";
+    hipLaunchKernelGGL((attn_decode3_kernel<R>), dim3(static_cast<unsigned>(pairs)), dim3(64 * nw),
+                       decode3_lds_bytes(R, nw), s, a);
+    return hipGetLastError();
+  }
+  // few pairs (long contexts, small batches): split the slots of each pair
+  // into chunks across wavefronts of their own, then merge the partials
+  if (kernel_name) *kernel_name = "attn_decode_splitk";
+  const int64_t want = std::max<int64_t>(1, target / pairs);
+  int chunk = static_cast<int>(((a.S + want - 1) / want + kDSub - 1) / kDSub * kDSub);
+  chunk = std::max(chunk, kDChunk);  // never more chunks than the workspace holds
+  const int nch = (a.S + chunk - 1) / chunk;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + static_cast<int64_t>(a.B) * a.nq * nch * HD;
+  hipLaunchKernelGGL((attn_decode2_kernel<R>), dim3(static_cast<unsigned>((pairs * nch + 3) / 4)), dim3(256), 0, s,
+                     a, nch, chunk, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t waves = static_cast<int64_t>(a.B) * a.nq;
+  hipLaunchKernelGGL((attn_decode_combine_kernel<bf16_t, HD>), dim3(static_cast<unsigned>((waves + 3) / 4)),
+                     dim3(256), 0, s, a, nch, chunk, part_o, part_ml);
+  return hipGetLastError();
+}
+
+// Generic decode (fp32, or hd = 64): attn_decode_kernel over 256-slot chunks
+// plus the merge.
 template <typename T, int HD>
-hipError_t launch_decode_t(const AttnArgs& a, void* ws, hipStream_t s) {
+hipError_t launch_decode_t(const AttnArgs& a, void* ws, hipStream_t s, const char** kernel_name) {
+  const int R = a.nq / a.nkv;
+  if (sizeof(T) == 2 && HD == 128) {
+    switch (R) {
+      case 1: return launch_decode_bf16<1>(a, ws, s, kernel_name);
+      case 2: return launch_decode_bf16<2>(a, ws, s, kernel_name);
+      case 4: return launch_decode_bf16<4>(a, ws, s, kernel_name);
+      case 8: return launch_decode_bf16<8>(a, ws, s, kernel_name);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (kernel_name) *kernel_name = "attn_decode_splitk";
   const int nch = decode_chunks(a.S);
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + static_cast<int64_t>(a.B) * a.nq * nch * HD;
-  const int R = a.nq / a.nkv;
   dim3 grid(a.B * a.nkv * nch);
-  if (sizeof(T) == 2 && HD == 128 && R <= 8) {
-    dim3 g2((a.B * a.nkv * nch + 3) / 4);
-    switch (R) {
-      case 1: hipLaunchKernelGGL((attn_decode2_kernel<1>), g2, dim3(256), 0, s, a, nch, part_o, part_ml); break;
-      case 2: hipLaunchKernelGGL((attn_decode2_kernel<2>), g2, dim3(256), 0, s, a, nch, part_o, part_ml); break;
-      case 4: hipLaunchKernelGGL((attn_decode2_kernel<4>), g2, dim3(256), 0, s, a, nch, part_o, part_ml); break;
-      default: hipLaunchKernelGGL((attn_decode2_kernel<8>), g2, dim3(256), 0, s, a, nch, part_o, part_ml); break;
-    }
-    hipError_t e2 = hipGetLastError();
-    if (e2 != hipSuccess) return e2;
-    const int64_t waves = static_cast<int64_t>(a.B) * a.nq;
-    hipLaunchKernelGGL((attn_decode_combine_kernel<T, HD>), dim3(static_cast<unsigned>((waves + 3) / 4)),
-                       dim3(256), 0, s, a, nch, part_o, part_ml);
-    return hipGetLastError();
-  }
   switch (R) {
     case 1: hipLaunchKernelGGL((attn_decode_kernel<T, HD, 1>), grid, dim3(256), 0, s, a, nch, part_o, part_ml); break;
     case 2: hipLaunchKernelGGL((attn_decode_kernel<T, HD, 2>), grid, dim3(256), 0, s, a, nch, part_o, part_ml); break;
@@ -735,7 +963,7 @@ hipError_t launch_decode_t(const AttnArgs& a, void* ws, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int64_t waves = static_cast<int64_t>(a.B) * a.nq;
   hipLaunchKernelGGL((attn_decode_combine_kernel<T, HD>), dim3(static_cast<unsigned>((waves + 3) / 4)),
-                     dim3(256), 0, s, a, nch, part_o, part_ml);
+                     dim3(256), 0, s, a, nch, kDChunk, part_o, part_ml);
   return hipGetLastError();
 }
 
@@ -768,10 +996,11 @@ hipError_t launch_attention(DType dt, const AttnArgs& a, void* ws, size_t ws_byt
   if (decode_supported(dt, a)) {
     if (ws_bytes < attention_workspace_bytes(dt, a.B, a.Tq, a.S, a.nq, a.nkv, a.hd))
       return hipErrorInvalidValue;
-    if (kernel_name) *kernel_name = "attn_decode_splitk";
     if (dt == DType::BF16)
-      return a.hd == 128 ? launch_decode_t<bf16_t, 128>(a, ws, s) : launch_decode_t<bf16_t, 64>(a, ws, s);
-    return a.hd == 128 ? launch_decode_t<float, 128>(a, ws, s) : launch_decode_t<float, 64>(a, ws, s);
+      return a.hd == 128 ? launch_decode_t<bf16_t, 128>(a, ws, s, kernel_name)
+                         : launch_decode_t<bf16_t, 64>(a, ws, s, kernel_name);
+    return a.hd == 128 ? launch_decode_t<float, 128>(a, ws, s, kernel_name)
+                       : launch_decode_t<float, 64>(a, ws, s, kernel_name);
   }
   if (flash_supported(dt, a)) {
     const int R = a.nq / a.nkv;

@@ -249,6 +249,47 @@ def test_decode_attention(nq, nkv, hd, dtype):
                                   np.repeat(to64(v[2, 0])[:, None], nq // nkv, axis=1))
 
 
+def decode_kernel_used(q, k, v, pos):
+    binding.profile_reset()
+    binding.profile_enable(True)
+    out = binding.gqa_attention(dev(q), dev(k), dev(v), dev(pos))
+    torch.cuda.synchronize()
+    names = binding.profile_collect()
+    binding.profile_enable(False)
+    return out, [n for n in names if n.startswith("attention/")]
+
+
+@pytest.mark.parametrize("nq,nkv", [(24, 24), (48, 24), (32, 8), (64, 8)])
+def test_decode_attention_many_sequences(nq, nkv):
+    """Enough (sequence, KV head) pairs for one workgroup per pair, merged in
+    LDS; ragged visible lengths (1 .. S) per sequence."""
+    B, S, hd = 24, 700, 128
+    q, k, v = attn_inputs(95, B, 1, S, nq, nkv, hd, "bf16")
+    lens = [700, 1, 33, 64, 65, 300, 511, 512, 513, 699, 2, 31, 32, 100, 257, 640, 7, 650, 690, 350, 128, 129, 96, 97]
+    pos = torch.tensor([[n - 1] for n in lens], dtype=torch.int32)
+    out, used = decode_kernel_used(q, k, v, pos)
+    assert used == ["attention/attn_decode_wg"]
+    ref = oracle.gqa_attention(to64(q), to64(k), to64(v), to64(pos).astype(np.int64))
+    report(f"decode wg {nq}/{nkv}", out, ref)
+    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, to64(v)))
+    one = lens.index(1)
+    np.testing.assert_array_equal(to64(out[one, 0]).reshape(nkv, nq // nkv, hd),
+                                  np.repeat(to64(v[one, 0])[:, None], nq // nkv, axis=1))
+
+
+def test_decode_attention_few_sequences_long_cache():
+    """Few pairs and a long cache: chunks spread over workgroups and merged
+    through the workspace."""
+    B, S, nq, nkv, hd = 2, 9000, 32, 8, 128
+    q, k, v = attn_inputs(96, B, 1, S, nq, nkv, hd, "bf16")
+    pos = torch.tensor([[8999], [4097]], dtype=torch.int32)
+    out, used = decode_kernel_used(q, k, v, pos)
+    assert used == ["attention/attn_decode_splitk"]
+    ref = oracle.gqa_attention(to64(q), to64(k), to64(v), to64(pos).astype(np.int64))
+    report("decode splitk long", out, ref)
+    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, to64(v)))
+
+
 # ---------------------------------------------------------------------------
 # SwiGLU FFN (GEMMs: MFMA tiles, split-K path, VALU path)
 # ---------------------------------------------------------------------------
