@@ -317,7 +317,7 @@ int llama_swiglu_ffn(const void* x, const void* w_gate, const void* w_up, const 
 namespace {
 
 struct BlockPlan {
-  size_t a, q, k, v, o, h, mact, attn, gemm, total;
+  size_t a, q, k, v, o, h, mact, attn, gemm, cs, total;
 };
 
 BlockPlan block_plan(int B, int T, int d, int nq, int nkv, int hd, int dff, int kv_cap, DType wdt,
@@ -339,7 +339,8 @@ BlockPlan block_plan(int B, int T, int d, int nq, int nkv, int hd, int dff, int 
   g = std::max(g, lb::gemm_workspace_bytes(wdt, static_cast<int>(M), dff, d, true));
   g = std::max(g, lb::gemm_workspace_bytes(wdt, static_cast<int>(M), d, dff, false));
   p.gemm = align_up(g);
-  p.total = p.a + p.q + p.k + p.v + p.o + p.h + p.mact + p.attn + p.gemm;
+  p.cs = align_up(M * (hd / 2) * 2 * sizeof(float));
+  p.total = p.a + p.q + p.k + p.v + p.o + p.h + p.mact + p.attn + p.gemm + p.cs;
   return p;
 }
 
@@ -407,6 +408,7 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
   void* mact = carve(p.mact);
   void* attn_ws = carve(p.attn);
   void* gemm_ws = carve(p.gemm);
+  float* rope_cs = reinterpret_cast<float*>(carve(p.cs));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const lb::RopeTable rope = make_rope(hd, rope_theta);
   const float feps = static_cast<float>(eps);
@@ -429,8 +431,11 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
     ep.kind = lb::EpiKind::Qkv; ep.out_dt = wdt;
     ep.q = q_buf; ep.k = k_buf; ep.v = v_buf; ep.positions = positions;
     ep.nq_hd = nq * hd; ep.nkv_hd = nkv * hd; ep.hd = hd; ep.seq_len = T; ep.kv_cap = kv_cap;
-    ep.rope = &rope;
+    ep.rope_cs = rope_cs;
     e = timed("qkv_rope", s, [&](const char** name) {
+      // the rotation angles' (cos, sin) per token and pair, then the GEMM
+      hipError_t er = lb::launch_rope_table(positions, M, hd, rope, wdt, rope_cs, s);
+      if (er != hipSuccess) return er;
       return lb::launch_gemm(wdt, a_buf, M, d, wqkv, (nq + 2 * nkv) * hd, false, ep, gemm_ws, p.gemm, s, name);
     });
     if (e != hipSuccess) return hip_fail(e, "llama_block_forward: qkv projection");

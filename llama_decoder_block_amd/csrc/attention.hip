@@ -118,6 +118,15 @@ constexpr int kKBytes = kFKeys * kKStride;
 constexpr int kVBytes = kFHd * kVStride;
 constexpr int kFBufBytes = kKBytes + kVBytes;
 
+#ifndef LB_FLASH_PRIO
+#define LB_FLASH_PRIO 0
+#endif
+#if LB_FLASH_PRIO
+#define FLASH_PRIO(p) __builtin_amdgcn_s_setprio(p)
+#else
+#define FLASH_PRIO(p) ((void)0)
+#endif
+
 template <int R>
 __global__ void __launch_bounds__(256, 2)
 attn_flash_kernel(AttnArgs a, int n_qtiles) {
@@ -169,38 +178,43 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
   const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * kFHd;
   const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * kFHd;
 
-  // global -> register staging: K: 4 rows x 16 B per thread; V: 4 slots x 8 hd
+  // global -> register staging: K: 4 rows x 16 B per thread; V: 4 slots x 8 hd.
+  // Loads go through buffer resources based at this (sequence, KV head):
+  // the lane's byte offset stays in a VGPR, the tile's in an SGPR.
   const int k_chunk = tid & 15, k_row = tid >> 4;     // rows k_row + 16 i
   const int v_kg = tid & 15, v_hc = tid >> 4;         // slots 4*v_kg..+3, hd 8*v_hc..+7
   u32x4 kreg[4], vreg[4];
-  // lane offsets (elements) of this thread's K rows / V slots within a tile
-  int koff[4], voff[4];
+  const uint32_t kv_bytes = static_cast<uint32_t>((static_cast<int64_t>(a.S - 1) * kvrow + kFHd) * 2);
+  const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kbase, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vbase, kv_bytes);
+  const uint32_t row_bytes = static_cast<uint32_t>(kvrow) * 2;
+  uint32_t koff[4], voff[4];  // byte offsets of this thread's K rows / V slots within a tile
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    koff[i] = (k_row + 16 * i) * static_cast<int>(kvrow) + k_chunk * 8;
-    voff[i] = (4 * v_kg + i) * static_cast<int>(kvrow) + v_hc * 8;
+    koff[i] = (k_row + 16 * i) * row_bytes + k_chunk * 16;
+    voff[i] = (4 * v_kg + i) * row_bytes + v_hc * 16;
   }
   auto gload = [&](int kt) {
     const int base = kt * kFKeys;
-    if (base + kFKeys <= a.S) {
-      // whole tile inside the cache: uniform tile base + lane offsets
-      const bf16_t* kt_k = kbase + static_cast<int64_t>(base) * kvrow;
-      const bf16_t* kt_v = vbase + static_cast<int64_t>(base) * kvrow;
+    if (base + kFKeys - 1 <= maxvis) {
+      const uint32_t soff = static_cast<uint32_t>(base) * row_bytes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kreg[i] = *reinterpret_cast<const u32x4*>(kt_k + koff[i]);
+      for (int i = 0; i < 4; ++i) kreg[i] = buffer_load16(krsrc, koff[i], soff);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = *reinterpret_cast<const u32x4*>(kt_v + voff[i]);
+      for (int i = 0; i < 4; ++i) vreg[i] = buffer_load16(vrsrc, voff[i], soff);
     } else {
-      // last, partial tile: clamp slots to the cache (masked anyway)
+      // the tile holding the workgroup's last visible slot: later slots are
+      // read as that slot (their weights are exactly 0, and a cache row past
+      // the written positions may hold anything, NaN included)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = min(base + k_row + 16 * i, a.S - 1);
-        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + j * kvrow + k_chunk * 8);
+        const uint32_t j = static_cast<uint32_t>(min(base + k_row + 16 * i, maxvis));
+        kreg[i] = buffer_load16(krsrc, j * row_bytes + k_chunk * 16, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = min(base + 4 * v_kg + i, a.S - 1);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + j * kvrow + v_hc * 8);
+        const uint32_t j = static_cast<uint32_t>(min(base + 4 * v_kg + i, maxvis));
+        vreg[i] = buffer_load16(vrsrc, j * row_bytes + v_hc * 16, 0);
       }
     }
   };
@@ -249,6 +263,7 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.f;
+    FLASH_PRIO(1);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
@@ -257,6 +272,7 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
             kb + (h2 * 32 + (lane & 31)) * kKStride + kk * 32 + half * 16);
         sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[h2], 0, 0, 0);
       }
+    FLASH_PRIO(0);
     // Raw-score maximum of the tile (the scale c > 0 preserves order); keys
     // past a query's position are masked only on tiles that reach the
     // diagonal of some row of this wavefront (wave-uniform test).
@@ -310,6 +326,7 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
     l_run += psum;
 
     // O^T += V^T P^T
+    FLASH_PRIO(1);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -325,6 +342,7 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
                                                             pf[h2][hh], oacc[d], 0, 0, 0);
         }
       }
+    FLASH_PRIO(0);
     if (kt + 1 < nkt) lstore(buf ^ 1);
     __syncthreads();
   }
@@ -976,8 +994,10 @@ bool decode_supported(DType dt, const AttnArgs& a) {
 
 bool flash_supported(DType dt, const AttnArgs& a) {
   const int R = a.nq / a.nkv;
+  // (the K/V buffer resources address one sequence's cache with 32-bit offsets)
   return dt == DType::BF16 && a.Tq > 1 && a.hd == kFHd &&
-         (R == 1 || R == 2 || R == 4 || R == 8);
+         (R == 1 || R == 2 || R == 4 || R == 8) &&
+         static_cast<int64_t>(a.S) * a.nkv * a.hd * 2 < (int64_t(1) << 31);
 }
 
 }  // namespace

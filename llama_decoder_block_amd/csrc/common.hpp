@@ -80,6 +80,18 @@ template <> struct Vec4<bf16_t> {
 };
 
 // ---------------------------------------------------------------------------
+// buffer loads: a 128-bit resource (base, size in bytes) in SGPRs, a per-lane
+// byte offset and a wave-uniform byte offset; reads past `bytes` return 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// ---------------------------------------------------------------------------
 // wavefront reductions (64 lanes)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {

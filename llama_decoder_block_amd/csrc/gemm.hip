@@ -634,11 +634,6 @@ struct BufOperands {
   int s1, s2;             // logical start rows of segments 1 and 2
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
-}
-
 template <bool DUAL, class Epi>
 __global__ void __launch_bounds__(256, 1)
 gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_n, Epi epi) {
@@ -1170,10 +1165,10 @@ hipError_t with_epi(const GemmEpi& e, F&& f) {
       if (e.out_dt == DType::F32)
         return f(EpiQkv<float>{static_cast<float*>(e.q), static_cast<float*>(e.k),
                                static_cast<float*>(e.v), e.positions, e.nq_hd, e.nkv_hd, e.hd,
-                               e.seq_len, e.kv_cap, *e.rope});
+                               e.seq_len, e.kv_cap, e.rope_cs});
       return f(EpiQkv<bf16_t>{static_cast<bf16_t*>(e.q), static_cast<bf16_t*>(e.k),
                               static_cast<bf16_t*>(e.v), e.positions, e.nq_hd, e.nkv_hd, e.hd,
-                              e.seq_len, e.kv_cap, *e.rope});
+                              e.seq_len, e.kv_cap, e.rope_cs});
     default:
       return hipErrorInvalidValue;
   }

@@ -79,7 +79,7 @@ struct EpiQkv {
   T* v;
   const int32_t* positions;
   int nq_hd, nkv_hd, hd, seq_len, kv_cap;
-  RopeTable rope;
+  const float* cs;  // [M, hd/2] (cos, sin) of each row's rotation angles (launch_rope_table)
 
   __device__ __forceinline__ T* dest(int m, int n, int pos) const {
     if (n < nq_hd) return q + static_cast<int64_t>(m) * nq_hd + n;
@@ -89,30 +89,35 @@ struct EpiQkv {
     if (kv_cap > 0) row = static_cast<int64_t>(m / seq_len) * kv_cap + pos;
     return (is_k ? k : v) + row * nkv_hd + nn;
   }
-  __device__ __forceinline__ void rotate(int n, int pos, float& a, float& b) const {
-    if (n < nq_hd + nkv_hd) {  // Q or K: rotate the pair; V is stored as is
-      float s, c;
-      rope_sincos_t<T>(pos, rope.inv_freq[(n % hd) >> 1], &s, &c);
-      const float ra = a * c - b * s;
-      b = a * s + b * c;
-      a = ra;
-    }
+  __device__ __forceinline__ const float* angle(int m, int n) const {
+    return cs + (static_cast<int64_t>(m) * (hd >> 1) + ((n % hd) >> 1)) * 2;
   }
   __device__ __forceinline__ void operator()(int m, int n, const float v4[4], int cnt) const {
-    const int pos = positions[m];
+    const int pos = kv_cap > 0 ? positions[m] : 0;
     float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+    const bool rot = n < nq_hd + nkv_hd;  // Q or K: rotate the pairs; V is stored as is
     if (cnt == 4 && (hd & 3) == 0) {
-      // four columns in one head of one segment: one 4-wide store
-      rotate(n, pos, v[0], v[1]);
-      rotate(n + 2, pos, v[2], v[3]);
+      // four columns (two pairs) in one head of one segment: one 4-wide store
+      if (rot) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(angle(m, n));
+        const float a0 = v[0] * t[0] - v[1] * t[1], b0 = v[0] * t[1] + v[1] * t[0];
+        const float a1 = v[2] * t[2] - v[3] * t[3], b1 = v[2] * t[3] + v[3] * t[2];
+        v[0] = a0; v[1] = b0; v[2] = a1; v[3] = b1;
+      }
       Vec4<T>::store(dest(m, n, pos), v);
       return;
     }
     for (int pr = 0; pr + 1 < cnt; pr += 2) {
-      rotate(n + pr, pos, v[pr], v[pr + 1]);
+      float a = v[pr], b = v[pr + 1];
+      if (rot) {
+        const f32x2 t = *reinterpret_cast<const f32x2*>(angle(m, n + pr));
+        const float ra = a * t[0] - b * t[1];
+        b = a * t[1] + b * t[0];
+        a = ra;
+      }
       T* d = dest(m, n + pr, pos);
-      st(d, v[pr]);
-      st(d + 1, v[pr + 1]);
+      st(d, a);
+      st(d + 1, b);
     }
   }
 };
@@ -167,7 +172,7 @@ struct GemmEpi {
   void* q; void* k; void* v;
   const int32_t* positions;
   int nq_hd, nkv_hd, hd, seq_len, kv_cap;
-  const RopeTable* rope;
+  const float* rope_cs;  // [M, hd/2] (cos, sin) table from launch_rope_table
 };
 
 // Workspace bytes the GEMM needs for a given problem (split-K partials).
@@ -186,6 +191,12 @@ hipError_t launch_rmsnorm(const void* x, const void* res, const void* gamma, voi
 
 hipError_t launch_rope(void* q, void* k, const int32_t* positions, int64_t n_tokens, int nq,
                        int nkv, int hd, const RopeTable& rope, DType dt, hipStream_t s);
+
+// cs[m][k] = (cos, sin) of positions[m] * inv_freq[k] for k < hd/2, fp32, the
+// angle reduced in fp64; accurate sin/cos for fp32 outputs (dt F32), the
+// hardware ones for bf16 outputs.  cs holds n_tokens * hd/2 float pairs.
+hipError_t launch_rope_table(const int32_t* positions, int64_t n_tokens, int hd, const RopeTable& rope,
+                             DType dt, float* cs, hipStream_t s);
 
 struct AttnArgs {
   const void* q;       // [B, Tq, nq, hd]

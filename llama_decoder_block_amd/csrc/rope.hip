@@ -76,7 +76,35 @@ hipError_t rope_one(T* x, const int32_t* positions, int64_t n_tokens, int heads,
   return hipGetLastError();
 }
 
+// One thread per (token row, pair): the rotation angle's (cos, sin).
+template <typename T>
+__global__ void __launch_bounds__(256)
+rope_table_kernel(const int32_t* __restrict__ positions, int64_t n_tokens, int half, RopeTable rope,
+                  f32x2* __restrict__ cs) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= n_tokens * half) return;
+  const int64_t tok = gid / half;
+  const int k = static_cast<int>(gid - tok * half);
+  float s, c;
+  rope_sincos_t<T>(positions[tok], rope.inv_freq[k], &s, &c);
+  cs[gid] = f32x2{c, s};
+}
+
 }  // namespace
+
+hipError_t launch_rope_table(const int32_t* positions, int64_t n_tokens, int hd, const RopeTable& rope,
+                             DType dt, float* cs, hipStream_t s) {
+  if (n_tokens == 0) return hipSuccess;
+  const int half = hd / 2;
+  const unsigned blocks = static_cast<unsigned>((n_tokens * half + 255) / 256);
+  if (dt == DType::F32)
+    hipLaunchKernelGGL((rope_table_kernel<float>), dim3(blocks), dim3(256), 0, s, positions, n_tokens, half, rope,
+                       reinterpret_cast<f32x2*>(cs));
+  else
+    hipLaunchKernelGGL((rope_table_kernel<bf16_t>), dim3(blocks), dim3(256), 0, s, positions, n_tokens, half, rope,
+                       reinterpret_cast<f32x2*>(cs));
+  return hipGetLastError();
+}
 
 hipError_t launch_rope(void* q, void* k, const int32_t* positions, int64_t n_tokens, int nq,
                        int nkv, int hd, const RopeTable& rope, DType dt, hipStream_t s) {

@@ -203,6 +203,27 @@ def test_flash_bf16_positions_with_cache():
     assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, to64(v)))
 
 
+@pytest.mark.parametrize("T", [64, 1])
+def test_attention_ignores_unwritten_cache_slots(T):
+    """Cache slots past every query's position may hold anything (here NaN and
+    inf): they get zero weight and must not reach the output (prefill of a
+    chunk, T = 64, and decode, T = 1)."""
+    B, S, nq, nkv, hd = 2, 300, 8, 2, 128
+    q, k, v = attn_inputs(61, B, T, S, nq, nkv, hd, "bf16")
+    pos = (torch.arange(T, dtype=torch.int32) + 100).repeat(B, 1)
+    pos[1] += 37
+    last = int(pos.max())
+    kd, vd = dev(k), dev(v)
+    kd[:, last + 1:] = float("nan")
+    vd[:, last + 1:] = float("inf")
+    vd[0, int(pos[0].max()) + 1:] = float("nan")
+    out = binding.gqa_attention(dev(q), kd, vd, dev(pos))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    ref = oracle.gqa_attention(to64(q), to64(k), to64(v), to64(pos).astype(np.int64))
+    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, to64(v)))
+
+
 def test_flash_gqa_equals_mha_on_repeated_kv():
     B, T, nq, nkv, hd = 1, 192, 8, 2, 128
     q, k, v = attn_inputs(70, B, T, T, nq, nkv, hd, "bf16")
