@@ -172,6 +172,11 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + half * 8);
+    // Consume the Q fragments here, so their loads are complete before the
+    // tile loop: otherwise the wait for them is placed inside the loop, where
+    // (the counter being in order) it also waits for the next tile's K/V.
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(qf[kk]));
   }
 
   const int64_t kvrow = static_cast<int64_t>(a.nkv) * kFHd;  // elements between slots
