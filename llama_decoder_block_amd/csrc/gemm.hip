@@ -1114,6 +1114,163 @@ splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t split_s
 }
 
 // ---------------------------------------------------------------------------
+// Skinny MFMA kernel for few token rows (decode: M <= 64).  The product is
+// bound by streaming the weights once, so the kernel is built around that
+// stream: a workgroup owns 64 weight rows (for the fused gate/up product 32
+// gate rows and the same 32 up rows) and all M <= 64 tokens over a K range
+// split four ways between its wavefronts.  Each wavefront works alone on its
+// K range: per step of 64 K elements it loads its 64 weight rows and the 64
+// token rows with whole 128-byte lines per row (eight lanes per row), one
+// step ahead into registers; stores them into its own LDS region (16-byte
+// chunks XOR-swizzled by (row / 2) % 8) and reads the MFMA fragments back,
+// so the next step's loads are in flight during this step's products.  The
+// four wavefronts' 64 x 64 tiles are then summed through LDS and the epilogue
+// (or, with a K split across workgroups, an fp32 partial store for
+// splitk_reduce_kernel) runs on whole rows.  Needs K / splits % 256 == 0.
+// ---------------------------------------------------------------------------
+constexpr int kSkStep = 64;  // K elements per step
+
+__device__ __forceinline__ int sk_idx(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
+
+template <bool DUAL, class Epi>
+__global__ void __launch_bounds__(256, 2)
+gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, int K, int ks, Epi epi) {
+  // per wavefront: 64 weight rows + 64 token rows of one step (128 B each);
+  // reused afterwards for the cross-wavefront sum
+  __shared__ u32x4 lds[4][2][64 * 8];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t row_bytes = static_cast<uint32_t>(K) * 2u;
+
+  // buffer resources of the two 32-row weight blocks of this workgroup
+  __amdgpu_buffer_rsrc_t wr[2];
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb) {
+    const bf16_t* base;
+    int left;
+    if (DUAL) {
+      const int f0 = blockIdx.x * 32;
+      base = op.w[fb] + static_cast<int64_t>(f0) * K;
+      left = op.wrows[fb] - f0;
+    } else {
+      const int r0 = blockIdx.x * 64 + fb * 32;
+      const int seg = r0 < op.s1 ? 0 : r0 < op.s2 ? 1 : 2;
+      const int start = seg == 0 ? 0 : seg == 1 ? op.s1 : op.s2;
+      base = op.w[seg] + static_cast<int64_t>(r0 - start) * K;
+      left = op.wrows[seg] - (r0 - start);
+    }
+    left = max(0, min(left, 32));
+    wr[fb] = make_rsrc(base, static_cast<uint32_t>(left) * row_bytes);
+  }
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, static_cast<uint32_t>(M) * row_bytes);
+
+  const int kw = ks / 4;  // K elements of this wavefront
+  const int k0 = blockIdx.z * ks + w * kw;
+  const int nsteps = kw / kSkStep;
+  // load pattern: instruction i covers rows 8i .. 8i+7, lane = (row % 8) * 8 + chunk
+  const int lrow = lane >> 3, lchunk = lane & 7;
+  const uint32_t voff = static_cast<uint32_t>(lrow) * row_bytes + lchunk * 16u;
+  struct Stage {
+    u32x4 w[8], x[8];
+  };
+  auto gload = [&](Stage& g, int step) {
+    const uint32_t soff = static_cast<uint32_t>(k0 + min(step, nsteps - 1) * kSkStep) * 2u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g.w[i] = buffer_load16(wr[i >> 2], voff + static_cast<uint32_t>(i & 3) * 8u * row_bytes, soff);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g.x[i] = buffer_load16(xr, voff + static_cast<uint32_t>(i) * 8u * row_bytes, soff);
+  };
+  u32x4* lw = lds[w][0];
+  u32x4* lx = lds[w][1];
+  auto lstore = [&](const Stage& g) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lw[sk_idx(i * 8 + lrow, lchunk)] = g.w[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lx[sk_idx(i * 8 + lrow, lchunk)] = g.x[i];
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[fb][tb][e] = 0.f;
+  const int fr = lane & 31, fh = lane >> 5;
+  auto compute = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb) a[fb] = __builtin_bit_cast(bf16x8, lw[sk_idx(fb * 32 + fr, 2 * i + fh)]);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) b[tb] = __builtin_bit_cast(bf16x8, lx[sk_idx(tb * 32 + fr, 2 * i + fh)]);
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fb], b[tb], acc[fb][tb], 0, 0, 0);
+    }
+  };
+  // The next step's loads are in flight while this step multiplies out of
+  // LDS.  LDS accesses of one wavefront execute in order, so a step's stores
+  // may follow the previous step's fragment reads without a barrier.  The
+  // load past the last step re-reads it (cache hits).
+  Stage g;
+  gload(g, 0);
+  lstore(g);
+  for (int st = 0; st < nsteps; ++st) {
+    gload(g, st + 1);
+    compute();
+    lstore(g);
+  }
+
+  // sum the four wavefronts' tiles: C register e is row (e/4)*8 + fh*4 + e%4
+  // of a 32-row block and token fr of a 32-token block.  The sum buffer is
+  // [wave][token][16 chunks of 4 rows], chunks XOR-swizzled by token % 16.
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(&lds[0][0][0]);
+  auto rix = [](int wv, int tok, int chunk) { return (wv * 64 + tok) * 16 + (chunk ^ (tok & 15)); };
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        red[rix(w, tb * 32 + fr, fb * 8 + j * 2 + fh)] =
+            f32x4{acc[fb][tb][4 * j], acc[fb][tb][4 * j + 1], acc[fb][tb][4 * j + 2], acc[fb][tb][4 * j + 3]};
+  __syncthreads();
+  const int m = tid >> 2, q = tid & 3;
+  if (m >= M) return;
+  auto sum4 = [&](int row) {
+    f32x4 v = red[rix(0, m, row >> 2)];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) v += red[rix(ww, m, row >> 2)];
+    return v;
+  };
+  if constexpr (DUAL) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int row = q * 8 + g * 4;
+      const int c = blockIdx.x * 32 + row;
+      if (c >= N) continue;
+      const f32x4 g4 = sum4(row), u4 = sum4(32 + row);
+      const float gv[4] = {g4[0], g4[1], g4[2], g4[3]};
+      const float uv[4] = {u4[0], u4[1], u4[2], u4[3]};
+      epi(m, c, gv, uv, min(4, N - c));
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int row = q * 16 + g * 4;
+      const int n = blockIdx.x * 64 + row;
+      if (n >= N) continue;
+      const f32x4 v4 = sum4(row);
+      const float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+      epi(m, n, v, min(4, N - n));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dispatch helpers
 // ---------------------------------------------------------------------------
 struct Plan {
@@ -1219,13 +1376,31 @@ BufOperands buf_operands(const bf16_t* x, const WSeg& w, int N, bool dual) {
   return op;
 }
 
+// The skinny kernel takes bf16 products with M <= 64 tokens, K a multiple of
+// 256 and weight segments starting on 32-row boundaries.
+bool skinny_shape(DType dt, int M, int K) { return dt == DType::BF16 && M <= 64 && K % 256 == 0; }
+
+// K splits across workgroups: until there are >= 384 workgroups (1.5 per
+// CU), keeping K / splits a multiple of 256.
+int skinny_splits(int n_logical, int K) {
+  const int nb = ceil_div(n_logical, 64);
+  int splits = 1;
+  while (nb * splits < 384 && K % (splits * 2 * 256) == 0) splits *= 2;
+  return splits;
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(DType dt, int M, int N, int K, bool dual) {
   Plan p = make_plan(dt, M, N, K, dual);
-  if (!p.mfma || p.splits <= 1) return 0;
   const int n_logical = dual ? 2 * N : N;
-  return static_cast<size_t>(p.splits) * M * n_logical * sizeof(float);
+  size_t need = 0;
+  if (p.mfma && p.splits > 1) need = static_cast<size_t>(p.splits) * M * n_logical * sizeof(float);
+  if (skinny_shape(dt, M, K)) {
+    const int sk = skinny_splits(n_logical, K);
+    if (sk > 1) need = std::max(need, static_cast<size_t>(sk) * M * n_logical * sizeof(float));
+  }
+  return need;
 }
 
 hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int N, bool dual,
@@ -1268,6 +1443,50 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
 
   const bf16_t* xp = static_cast<const bf16_t*>(X);
   auto rows = make_rows<bf16_t>(W, K);
+  if (skinny_shape(dt, M, K) && rs_ok(W, N, dual)) {
+    const int n_logical = dual ? 2 * N : N;
+    const int splits = skinny_splits(n_logical, K);
+    const int ks = K / splits;
+    if (splits == 1) {
+      if (kernel_name) *kernel_name = dual ? "gemm_skinny_gate_up_silu" : "gemm_skinny";
+      BufOperands op = buf_operands(xp, W, N, dual);
+      dim3 grid(ceil_div(n_logical, 64), 1, 1);
+      if (dual)
+        return with_silu(epi, [&](auto e) {
+          hipLaunchKernelGGL((gemm_skinny_kernel<true, decltype(e)>), grid, dim3(256), 0, s, xp, op, M, N, K, ks, e);
+          return hipGetLastError();
+        });
+      return with_epi(epi, [&](auto e) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<false, decltype(e)>), grid, dim3(256), 0, s, xp, op, M, N, K, ks, e);
+        return hipGetLastError();
+      });
+    }
+    // fp32 partials over the logical rows (gate rows then up rows when dual)
+    const size_t need = static_cast<size_t>(splits) * M * n_logical * sizeof(float);
+    if (ws == nullptr || ws_bytes < need) return hipErrorInvalidValue;
+    if (kernel_name) *kernel_name = dual ? "gemm_skinny_splitk_gate_up" : "gemm_skinny_splitk";
+    float* part = static_cast<float*>(ws);
+    const int64_t split_stride = static_cast<int64_t>(M) * n_logical;
+    EpiPartial pe{part, n_logical, split_stride};
+    BufOperands op = buf_operands(xp, W, n_logical, false);
+    hipLaunchKernelGGL((gemm_skinny_kernel<false, EpiPartial>), dim3(ceil_div(n_logical, 64), 1, splits), dim3(256),
+                       0, s, xp, op, M, n_logical, K, ks, pe);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t threads = static_cast<int64_t>(M) * ceil_div(N, 4);
+    const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
+    if (dual)
+      return with_silu(epi, [&](auto e) {
+        hipLaunchKernelGGL((splitk_reduce_kernel<true, decltype(e)>), dim3(blocks), dim3(256), 0, s,
+                           part, splits, split_stride, M, N, n_logical, e);
+        return hipGetLastError();
+      });
+    return with_epi(epi, [&](auto e) {
+      hipLaunchKernelGGL((splitk_reduce_kernel<false, decltype(e)>), dim3(blocks), dim3(256), 0, s,
+                         part, splits, split_stride, M, N, n_logical, e);
+      return hipGetLastError();
+    });
+  }
   if (p.splits <= 1) {
     if (kernel_name) *kernel_name = dual ? "gemm_mfma_gate_up_silu" : "gemm_mfma";
     if (p.big && LB_GEMM_DMA64) {
