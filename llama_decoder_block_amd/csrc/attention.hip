@@ -113,7 +113,7 @@ constexpr int kFHd = 128;
 constexpr int kFRows = 128;              // query rows per workgroup
 constexpr int kFKeys = 64;               // key slots per tile
 constexpr int kKStride = kFHd * 2 + 16;  // bytes per K row in LDS (padded)
-constexpr int kVStride = kFKeys * 2 + 8; // bytes per V^T row in LDS (padded)
+constexpr int kVStride = kFKeys * 2 + 16; // bytes per V^T row in LDS (padded, 16-byte aligned)
 constexpr int kKBytes = kFKeys * kKStride;
 constexpr int kVBytes = kFHd * kVStride;
 constexpr int kFBufBytes = kKBytes + kVBytes;
@@ -230,15 +230,20 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<u32x4*>(kb + (k_row + 16 * i) * kKStride + k_chunk * 16) = kreg[i];
     // transpose 4 slots x 8 hd into 8 rows (hd) of 4 slots: output word
-    // (slot pair, hd e) takes the same 16-bit half of two input words
+    // (slot pair, hd e) takes the same 16-bit half of two input words.
+    // Within each 16-slot block the 4-slot groups are stored in the order
+    // 0, 2, 1, 3, so that the 8 slots one lane multiplies in the PV product
+    // (4s..4s+3 and 8+4s..8+4s+3 for lane half s) are 16 contiguous bytes.
+    const int v_grp = v_kg & 3;
+    const int v_pos = ((v_kg >> 2) * 16 + ((v_grp & 1) << 3) + ((v_grp & 2) << 1)) * 2;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const u32x2 lo = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u),
                         __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u)};
       const u32x2 hi = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u),
                         __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u)};
-      *reinterpret_cast<u32x2*>(vb + (v_hc * 8 + 2 * w) * kVStride + v_kg * 8) = lo;
-      *reinterpret_cast<u32x2*>(vb + (v_hc * 8 + 2 * w + 1) * kVStride + v_kg * 8) = hi;
+      *reinterpret_cast<u32x2*>(vb + (v_hc * 8 + 2 * w) * kVStride + v_pos) = lo;
+      *reinterpret_cast<u32x2*>(vb + (v_hc * 8 + 2 * w + 1) * kVStride + v_pos) = hi;
     }
   };
 
@@ -336,13 +341,11 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int s0 = h2 * 32 + hh * 16 + half * 4;
+        const int s0 = h2 * 32 + hh * 16 + half * 8;  // stored position of this lane's 8 slots
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const uint8_t* vr = vb + (d * 32 + (lane & 31)) * kVStride;
-          u32x2 lo = *reinterpret_cast<const u32x2*>(vr + s0 * 2);
-          u32x2 hi = *reinterpret_cast<const u32x2*>(vr + (s0 + 8) * 2);
-          u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
+          const u32x4 vv = *reinterpret_cast<const u32x4*>(vr + s0 * 2);
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
                                                             pf[h2][hh], oacc[d], 0, 0, 0);
         }
