@@ -4,21 +4,20 @@
 // "Production PyTorch Implementation"), followed by a fused epilogue:
 // RoPE + Q/K/V (cache) stores, SiLU(gate) * up, residual add, or a plain store.
 //
-// gemm_mfma_kernel: bf16 operands on the CDNA4 matrix cores
-//   (v_mfma_f32_32x32x16_bf16), fp32 accumulation.  Four wavefronts in a 2x2
-//   arrangement; each owns a (BN/2) x (BM/2) block of the output as 32x32
-//   MFMA tiles.  The weight tile is the MFMA "A" operand and the activation
-//   tile the "B" operand, so each lane ends up with four consecutive output
-//   columns (feature index) of one token row: RoPE pairs and 4-wide stores
-//   stay inside a lane.  K is walked in steps of 64 through two LDS buffers;
-//   the next step's global loads are in flight while the current step's
-//   MFMAs run.  LDS rows are 128 B (64 bf16) with the 16-byte chunk index
-//   XOR-swizzled by the row pair so that fragment reads do not collide in banks.
-// gemm_valu_kernel: generic fp32-accumulating kernel for the fp32 path and
-//   for shapes the MFMA kernel does not take (K % 8 != 0).
-// split-K: for few token rows (decode) the MFMA kernel writes fp32 partial
-//   sums per K-slice and splitk_reduce_kernel sums them and applies the
-//   epilogue, so enough workgroups stream the weights.
+// Kernels (bf16 operands on the CDNA4 matrix cores, v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation; the weight tile is the MFMA "A" operand and the
+// activations the "B" operand, so each lane holds four consecutive output
+// features of one token: RoPE pairs and 4-wide stores stay inside a lane):
+// gemm_mfma_rs_kernel: prefill (M >= 512, K % 64 == 0, weight segments on
+//   32-row boundaries).  256x256 tiles, one wavefront per SIMD owning 128x128,
+//   register-staged buffer loads two K steps ahead, XOR-swizzled LDS.
+// gemm_skinny_kernel: decode (M <= 64, K % 256 == 0): streams the weights once
+//   with whole-line loads, K split over the wavefronts and summed in LDS.
+// gemm_mfma_kernel: generic tiles (64x64 .. 256x256) for every other bf16
+//   shape; with few rows it writes fp32 partial sums per K slice and
+//   splitk_reduce_kernel sums them and applies the epilogue.
+// gemm_valu_kernel: fp32-accumulating VALU kernel for the fp32 path and for
+//   K % 8 != 0.
 #include <type_traits>
 
 #include "common.hpp"
@@ -76,18 +75,6 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int 
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;
 
-#ifndef LB_GEMM_FOUR_WAVES
-#define LB_GEMM_FOUR_WAVES 1
-#endif
-#ifndef LB_GEMM_RS
-#define LB_GEMM_RS 1
-#endif
-#ifndef LB_GEMM_DMA64
-#define LB_GEMM_DMA64 0
-#endif
-#ifndef LB_GEMM_NST
-#define LB_GEMM_NST 4
-#endif
 
 // LDS tile rows are 128 B (64 bf16 of K).  gfx950 serves a 16-byte-per-lane
 // LDS read 16 lanes (256 B, all 64 banks) at a time; a fragment read has 16
@@ -248,162 +235,6 @@ gemm_mfma_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, in
 // clamped on load and dropped by the epilogue.  Fragments of the next
 // 16-wide K slice are read from LDS while the current slice's MFMAs run.
 // ---------------------------------------------------------------------------
-template <bool DUAL, class Epi>
-__global__ void __launch_bounds__(512, 2)
-gemm_mfma8_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, int K,
-                  int tiles_m, int tiles_n, Epi epi) {
-  constexpr int BN = 256, BM = 256;
-  constexpr int WN = 128, WM = 64;
-  constexpr int TN = 4, TM = 2;
-  constexpr int LD_IT = 4;  // 16-byte loads per thread per operand per K step
-  __shared__ u32x4 lds[2][(BN + BM) * 8];
-
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wave_n = wid & 1, wave_m = wid >> 1;
-  const int out_n0 = tn * (DUAL ? BN / 2 : BN);
-  const int m0 = tm * BM;
-  const int KT = K / kBK;
-
-  const int chunk = tid & 7, rbase = tid >> 3;  // rows rbase + 64 i
-  const bf16_t* wsrc[LD_IT];
-  const bf16_t* xsrc[LD_IT];
-#pragma unroll
-  for (int i = 0; i < LD_IT; ++i) {
-    const int r = rbase + 64 * i;
-    const bf16_t* p;
-    if constexpr (DUAL) {
-      // LDS rows [0,128): wave_n 0 (gate 0..63, up 0..63); [128,256): wave_n 1
-      const int wv = r / WN, rr = r % WN;
-      const bool up = rr >= WN / 2;
-      const int c = min(out_n0 + wv * (WN / 2) + (rr % (WN / 2)), N - 1);
-      p = (up ? W.p[1] : W.p[0]) + static_cast<int64_t>(c) * W.ld;
-    } else {
-      p = W.row(min(out_n0 + r, N - 1));
-    }
-    wsrc[i] = p + chunk * 8;
-    xsrc[i] = X + static_cast<int64_t>(min(m0 + r, M - 1)) * K + chunk * 8;
-  }
-
-  // two register staging sets: the loads of K steps kt+1 and kt+2 are in
-  // flight while step kt computes (hides memory latency of ~2 K steps)
-  u32x4 wreg[2][LD_IT], xreg[2][LD_IT];
-  auto gload = [&](int kt, auto S) {
-    constexpr int st = decltype(S)::value;
-#pragma unroll
-    for (int i = 0; i < LD_IT; ++i) wreg[st][i] = *reinterpret_cast<const u32x4*>(wsrc[i] + kt * kBK);
-#pragma unroll
-    for (int i = 0; i < LD_IT; ++i) xreg[st][i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kt * kBK);
-  };
-  auto lstore = [&](int buf, auto S) {
-    constexpr int st = decltype(S)::value;
-#pragma unroll
-    for (int i = 0; i < LD_IT; ++i) lds[buf][lds_idx(rbase + 64 * i, chunk)] = wreg[st][i];
-#pragma unroll
-    for (int i = 0; i < LD_IT; ++i) lds[buf][BN * 8 + lds_idx(rbase + 64 * i, chunk)] = xreg[st][i];
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int a = 0; a < TN; ++a)
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
-
-  const int frag_row = lane & 31, frag_half = lane >> 5;
-  int arow[TN], brow[TM];
-#pragma unroll
-  for (int a = 0; a < TN; ++a) arow[a] = wave_n * WN + a * 32 + frag_row;
-#pragma unroll
-  for (int b = 0; b < TM; ++b) brow[b] = BN + wave_m * WM + b * 32 + frag_row;
-
-  auto compute = [&](int buf) {
-    bf16x8 af[2][TN], bf[2][TM];
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-      af[0][a] = __builtin_bit_cast(bf16x8, lds[buf][lds_idx(arow[a], frag_half)]);
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-      bf[0][b] = __builtin_bit_cast(bf16x8, lds[buf][lds_idx(brow[b], frag_half)]);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < kBK / 16) {
-        const int ch = (kk + 1) * 2 + frag_half;
-#pragma unroll
-        for (int a = 0; a < TN; ++a)
-          af[cur ^ 1][a] = __builtin_bit_cast(bf16x8, lds[buf][lds_idx(arow[a], ch)]);
-#pragma unroll
-        for (int b = 0; b < TM; ++b)
-          bf[cur ^ 1][b] = __builtin_bit_cast(bf16x8, lds[buf][lds_idx(brow[b], ch)]);
-      }
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][a], bf[cur][b], acc[a][b], 0, 0, 0);
-    }
-  };
-
-  // K steps in pairs so that staging set and LDS buffer indices are static:
-  // even steps compute LDS buffer 0 / refill set 0, odd steps buffer 1 / set 1.
-  gload(0, S0{});
-  if (KT > 1) gload(1, S1{});
-  lstore(0, S0{});
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    if (kt + 2 < KT) gload(kt + 2, S0{});
-    compute(0);
-    lstore(1, S1{});
-    __syncthreads();
-    if (kt + 3 < KT) gload(kt + 3, S1{});
-    compute(1);
-    if (kt + 2 < KT) lstore(0, S0{});
-    __syncthreads();
-  }
-  if (kt < KT) compute(0);
-
-#pragma unroll
-  for (int b = 0; b < TM; ++b) {
-    const int m = m0 + wave_m * WM + b * 32 + frag_row;
-    if (m >= M) continue;
-    if constexpr (DUAL) {
-#pragma unroll
-      for (int a = 0; a < TN / 2; ++a)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = out_n0 + wave_n * (WN / 2) + a * 32 + j * 8 + frag_half * 4;
-          if (c >= N) continue;
-          float g[4], u[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            g[i] = acc[a][b][j * 4 + i];
-            u[i] = acc[a + TN / 2][b][j * 4 + i];
-          }
-          epi(m, c, g, u, min(4, N - c));
-        }
-    } else {
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4;
-          if (n >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
-          epi(m, n, v, min(4, N - n));
-        }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // MFMA kernel, large tiles, direct-to-LDS staging ("dma" kernel).
 // 256 x 256 output tile, four wavefronts (one per SIMD) in a 2 x 2 grid, each
 // owning 128 x 128 as 4 x 4 tiles of 32 x 32 (accumulators in AGPRs).
@@ -420,196 +251,6 @@ gemm_mfma8_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, i
 // are read before the end-of-stage barrier (that stage was confirmed complete
 // one barrier earlier), so the barrier does not idle the matrix cores.
 // Requires K % 32 == 0.
-// ---------------------------------------------------------------------------
-constexpr int kDmaBK = 32;
-
-__device__ __forceinline__ int dma_lds_off(int row, int chunk) {  // bytes within a stage operand
-  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-template <bool DUAL, int NST, class Epi>
-__global__ void __launch_bounds__(256, 1)
-gemm_mfma_dma_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, int K,
-                     int tiles_m, int tiles_n, Epi epi) {
-  constexpr int BN = 256, BM = 256, WN = 128, WM = 128, TN = 4, TM = 4;
-  constexpr int OP_BYTES = 256 * 64;            // one operand of one stage (16 KB)
-  constexpr int STAGE_BYTES = 2 * OP_BYTES;     // weights then activations
-  constexpr int LOADS = 8;                      // DMA instructions per wave per stage
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE_BYTES];
-
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave_n = wid & 1, wave_m = wid >> 1;
-  const int out_n0 = tn * (DUAL ? BN / 2 : BN);
-  const int m0 = tm * BM;
-  const int KT = K / kDmaBK;
-
-  // Copy assignment: wave w, instruction j (0..3) fills rows (4w + j)*16 ..
-  // +15 of the weight tile (and, for j in 4..7, of the activation tile).
-  // Lane i covers row +i/4, LDS chunk i%4, i.e. global chunk (i%4)^((row/4)%4).
-  const bf16_t* src[LOADS];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = (wid * 4 + j) * 16 + (lane >> 2);
-    const int gchunk = (lane & 3) ^ ((r >> 2) & 3);
-    const bf16_t* wp;
-    if constexpr (DUAL) {
-      const int wv = r / WN, rr = r % WN;
-      const bool up = rr >= WN / 2;
-      const int c = min(out_n0 + wv * (WN / 2) + (rr % (WN / 2)), N - 1);
-      wp = (up ? W.p[1] : W.p[0]) + static_cast<int64_t>(c) * W.ld;
-    } else {
-      wp = W.row(min(out_n0 + r, N - 1));
-    }
-    src[j] = wp + gchunk * 8;
-    src[4 + j] = X + static_cast<int64_t>(min(m0 + r, M - 1)) * K + gchunk * 8;
-  }
-  auto issue_stage = [&](int kt) {
-    uint8_t* base = lds + (kt % NST) * STAGE_BYTES;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      uint8_t* dst = base + (j >= 4 ? OP_BYTES : 0) + ((wid * 4 + (j & 3)) * 16) * 64;
-      __builtin_amdgcn_global_load_lds(src[j] + kt * kDmaBK, dst, 16, 0, 0);
-    }
-  };
-
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int a = 0; a < TN; ++a)
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
-
-  const int frag_row = lane & 31, frag_half = lane >> 5;
-  int aoff[TN], boff[TM];
-  bf16x8 fa[2][TN], fb[2][TM];
-  auto read_frags = [&](int kt, int sub, auto F) {
-    constexpr int f = decltype(F)::value;
-    const uint8_t* base = lds + (kt % NST) * STAGE_BYTES;
-    const int ch = sub * 2 + frag_half;
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-      fa[f][a] = *reinterpret_cast<const bf16x8*>(base + dma_lds_off(wave_n * WN + a * 32 + frag_row, ch));
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-      fb[f][b] = *reinterpret_cast<const bf16x8*>(base + OP_BYTES + dma_lds_off(wave_m * WM + b * 32 + frag_row, ch));
-  };
-  (void)aoff; (void)boff;
-  auto mfmas = [&](auto F) {
-    constexpr int f = decltype(F)::value;
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-#pragma unroll
-      for (int b = 0; b < TM; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][a], fb[f][b], acc[a][b], 0, 0, 0);
-  };
-  using F0 = std::integral_constant<int, 0>;
-  using F1 = std::integral_constant<int, 1>;
-
-  // MFMAs of one sub-step in two parts so that LDS reads can be issued after
-  // the first few have started
-  auto mfmas_part = [&](auto F, auto LO, auto HI) {
-    constexpr int f = decltype(F)::value;
-    constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
-#pragma unroll
-    for (int t = lo; t < hi; ++t)
-      acc[t / TM][t % TM] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][t / TM], fb[f][t % TM], acc[t / TM][t % TM], 0, 0, 0);
-  };
-  using P0 = std::integral_constant<int, 0>;
-  using P4 = std::integral_constant<int, 4>;
-  using P16 = std::integral_constant<int, 16>;
-  // Barrier without the implied memory-counter waits of __syncthreads():
-  // the copies of later stages stay in flight across it.  The memory clobber
-  // keeps the compiler from moving LDS accesses across it.
-  auto barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // prologue: stages 0 .. NST-2 in flight; stages 0 and 1 complete
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < KT) issue_stage(s);
-  if (KT >= NST - 1) wait_vmcnt<LOADS * (NST - 3)>();
-  else wait_vmcnt<0>();
-  barrier();
-  read_frags(0, 0, F0{});
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool issue = kt + NST - 1 < KT;
-    if (issue) issue_stage(kt + NST - 1);
-    // sub-step 0 (fragments in set 0); read sub-step 1 into set 1
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas_part(F0{}, P0{}, P4{});
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(kt, 1, F1{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas_part(F0{}, P4{}, P16{});
-    __builtin_amdgcn_sched_barrier(0);
-    // sub-step 1 (set 1); read sub-step 0 of stage kt+1 into set 0 (that
-    // stage was confirmed complete at the previous barrier)
-    mfmas_part(F1{}, P0{}, P4{});
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < KT) read_frags(kt + 1, 0, F0{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas_part(F1{}, P4{}, P16{});
-    // stage kt+2 complete for this wave (newer stages may stay in flight),
-    // then the barrier publishes it and frees stage kt's buffer
-    if (issue) wait_vmcnt<LOADS * (NST - 3)>();
-    else wait_vmcnt<0>();
-    barrier();
-  }
-
-  // epilogue: register e of a 32x32 tile is feature row (e/4)*8 + half*4 + e%4
-  // of the weight operand and token column lane%32
-#pragma unroll
-  for (int b = 0; b < TM; ++b) {
-    const int m = m0 + wave_m * WM + b * 32 + frag_row;
-    if (m >= M) continue;
-    if constexpr (DUAL) {
-#pragma unroll
-      for (int a = 0; a < TN / 2; ++a)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = out_n0 + wave_n * (WN / 2) + a * 32 + j * 8 + frag_half * 4;
-          if (c >= N) continue;
-          float g[4], u[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            g[i] = acc[a][b][j * 4 + i];
-            u[i] = acc[a + TN / 2][b][j * 4 + i];
-          }
-          epi(m, c, g, u, min(4, N - c));
-        }
-    } else {
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4;
-          if (n >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
-          epi(m, n, v, min(4, N - n));
-        }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // MFMA kernel, large tiles, register-staged buffer loads ("rs" kernel).
 // 256 x 256 output tile, four wavefronts (one per SIMD) in a 2 x 2 grid, each
@@ -800,187 +441,6 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
     kstep(kt + 1, I1{}, I0{}, I1{});
   }
   if (kt < KT) kstep(kt, I0{}, I1{}, I0{});
-
-  // epilogue: register e of a 32x32 tile is feature row (e/4)*8 + half*4 + e%4
-  // of the weight operand and token column lane%32
-#pragma unroll
-  for (int b = 0; b < TM; ++b) {
-    const int m = m0 + wave_m * WM + b * 32 + frag_row;
-    if (m >= M) continue;
-    if constexpr (DUAL) {
-#pragma unroll
-      for (int a = 0; a < TN / 2; ++a)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = out_n0 + wave_n * (WN / 2) + a * 32 + j * 8 + frag_half * 4;
-          if (c >= N) continue;
-          float g[4], u[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            g[i] = acc[a][b][j * 4 + i];
-            u[i] = acc[a + TN / 2][b][j * 4 + i];
-          }
-          epi(m, c, g, u, min(4, N - c));
-        }
-    } else {
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4;
-          if (n >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
-          epi(m, n, v, min(4, N - n));
-        }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// MFMA kernel, large tiles, direct-to-LDS copies of 64-wide K steps
-// ("dma64").  256 x 256 output tile, four wavefronts (one per SIMD), each
-// owning 128 x 128 as 4 x 4 tiles of 32 x 32 with AGPR accumulators.  Each
-// global_load_lds_dwordx4 copies 8 whole 128-byte rows (one cache line each)
-// into LDS, so no registers stage the tiles and the compiler inserts no
-// waits for them: the vmcnt waits below are explicit.  Two 64 KB stage
-// buffers: the copy of step kt+1 is issued as soon as the barrier of step
-// kt-1 frees its buffer and must land before the barrier of step kt.  Inside
-// a step the next 16-wide sub-step's fragments are read after the first 4
-// MFMAs of the current one; the barrier sits half-way through the last
-// sub-step's MFMAs, after which the first fragments of step kt+1 are read.
-// LDS rows are 128 B with the chunk XOR (row/2)%8 (conflict-free reads).
-// Requires K % 64 == 0.
-// ---------------------------------------------------------------------------
-template <bool DUAL, class Epi>
-__global__ void __launch_bounds__(256, 1)
-gemm_mfma_dma64_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, int K,
-                       int tiles_m, int tiles_n, Epi epi) {
-  constexpr int BN = 256, BM = 256, WN = 128, WM = 128, TN = 4, TM = 4;
-  constexpr int OP_BYTES = 256 * 128;           // one operand of one step (32 KB)
-  constexpr int STAGE_BYTES = 2 * OP_BYTES;
-  constexpr int LOADS = 16;                     // copies per wavefront per step
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE_BYTES];
-
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave_n = wid & 1, wave_m = wid >> 1;
-  const int out_n0 = tn * (DUAL ? BN / 2 : BN);
-  const int m0 = tm * BM;
-  const int KT = K / kBK;
-
-  // wavefront w, copy j (0..7) fills rows (8w + j)*8 .. +7 of the weight tile
-  // (j+8: of the activation tile); lane i covers row +i/8, LDS chunk i%8,
-  // read from global chunk (i%8) ^ ((row/2)%8).
-  const int rsub = lane >> 3, lchunk = lane & 7;
-  const bf16_t* src[LOADS];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (wid * 8 + j) * 8 + rsub;
-    const int gchunk = lchunk ^ ((r >> 1) & 7);
-    const bf16_t* wp;
-    if constexpr (DUAL) {
-      const int wv = r / WN, rr = r % WN;
-      const bool up = rr >= WN / 2;
-      const int c = min(out_n0 + wv * (WN / 2) + (rr % (WN / 2)), N - 1);
-      wp = (up ? W.p[1] : W.p[0]) + static_cast<int64_t>(c) * W.ld;
-    } else {
-      wp = W.row(min(out_n0 + r, N - 1));
-    }
-    src[j] = wp + gchunk * 8;
-    src[8 + j] = X + static_cast<int64_t>(min(m0 + r, M - 1)) * K + gchunk * 8;
-  }
-  auto issue_step = [&](int kt) {
-    uint8_t* base = lds + (kt & 1) * STAGE_BYTES;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      uint8_t* dst = base + (j >= 8 ? OP_BYTES : 0) + ((wid * 8 + (j & 7)) * 8) * 128;
-      __builtin_amdgcn_global_load_lds(src[j] + kt * kBK, dst, 16, 0, 0);
-    }
-  };
-
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int a = 0; a < TN; ++a)
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
-
-  const int frag_row = lane & 31, frag_half = lane >> 5;
-  bf16x8 fa[2][TN], fb[2][TM];
-  auto read_frags = [&](int kt, int sub, auto F) {
-    constexpr int f = decltype(F)::value;
-    const uint8_t* base = lds + (kt & 1) * STAGE_BYTES;
-    const int ch = sub * 2 + frag_half;
-#pragma unroll
-    for (int a = 0; a < TN; ++a) {
-      const int r = wave_n * WN + a * 32 + frag_row;
-      fa[f][a] = *reinterpret_cast<const bf16x8*>(base + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
-    }
-#pragma unroll
-    for (int b = 0; b < TM; ++b) {
-      const int r = wave_m * WM + b * 32 + frag_row;
-      fb[f][b] = *reinterpret_cast<const bf16x8*>(base + OP_BYTES + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
-    }
-  };
-  auto mfmas = [&](auto F, auto LO, auto HI) {
-    constexpr int f = decltype(F)::value;
-    constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
-#pragma unroll
-    for (int t = lo; t < hi; ++t)
-      acc[t / TM][t % TM] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][t / TM], fb[f][t % TM], acc[t / TM][t % TM], 0, 0, 0);
-  };
-  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-  // explicit waits: copies (vmcnt) and this wave's LDS reads (lgkmcnt), then
-  // a barrier without the compiler-implied full memory drain
-  auto barrier = [&]() {
-    fence();
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    fence();
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I4 = std::integral_constant<int, 4>;
-  using I8 = std::integral_constant<int, 8>;
-  using I16 = std::integral_constant<int, 16>;
-
-  issue_step(0);
-  barrier();
-  read_frags(0, 0, I0{});
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) issue_step(kt + 1);
-    fence();
-    mfmas(I0{}, I0{}, I4{});
-    fence();
-    read_frags(kt, 1, I1{});
-    fence();
-    mfmas(I0{}, I4{}, I16{});
-    fence();
-    mfmas(I1{}, I0{}, I4{});
-    fence();
-    read_frags(kt, 2, I0{});
-    fence();
-    mfmas(I1{}, I4{}, I16{});
-    fence();
-    mfmas(I0{}, I0{}, I4{});
-    fence();
-    read_frags(kt, 3, I1{});
-    fence();
-    mfmas(I0{}, I4{}, I16{});
-    fence();
-    mfmas(I1{}, I0{}, I8{});
-    barrier();
-    if (more) read_frags(kt + 1, 0, I0{});
-    fence();
-    mfmas(I1{}, I8{}, I16{});
-    fence();
-  }
 
   // epilogue: register e of a 32x32 tile is feature row (e/4)*8 + half*4 + e%4
   // of the weight operand and token column lane%32
@@ -1489,23 +949,7 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
   }
   if (p.splits <= 1) {
     if (kernel_name) *kernel_name = dual ? "gemm_mfma_gate_up_silu" : "gemm_mfma";
-    if (p.big && LB_GEMM_DMA64) {
-      const int tiles_m = ceil_div(M, 256);
-      const int tiles_n = ceil_div(N, dual ? 128 : 256);
-      dim3 grid(tiles_m * tiles_n);
-      if (dual)
-        return with_silu(epi, [&](auto e) {
-          hipLaunchKernelGGL((gemm_mfma_dma64_kernel<true, decltype(e)>), grid, dim3(256), 0, s, xp, rows, M, N,
-                             K, tiles_m, tiles_n, e);
-          return hipGetLastError();
-        });
-      return with_epi(epi, [&](auto e) {
-        hipLaunchKernelGGL((gemm_mfma_dma64_kernel<false, decltype(e)>), grid, dim3(256), 0, s, xp, rows, M, N, K,
-                           tiles_m, tiles_n, e);
-        return hipGetLastError();
-      });
-    }
-    if (p.big && LB_GEMM_RS && rs_ok(W, N, dual)) {
+    if (p.big && rs_ok(W, N, dual)) {
       const int tiles_m = ceil_div(M, 256);
       const int tiles_n = ceil_div(N, dual ? 128 : 256);
       dim3 grid(tiles_m * tiles_n);
@@ -1518,38 +962,6 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
         });
       return with_epi(epi, [&](auto e) {
         hipLaunchKernelGGL((gemm_mfma_rs_kernel<false, decltype(e)>), grid, dim3(256), 0, s, op, M, N, K,
-                           tiles_m, tiles_n, e);
-        return hipGetLastError();
-      });
-    }
-    if (p.big && LB_GEMM_FOUR_WAVES) {
-      const int tiles_m = ceil_div(M, 256);
-      const int tiles_n = ceil_div(N, dual ? 128 : 256);
-      dim3 grid(tiles_m * tiles_n);
-      if (dual)
-        return with_silu(epi, [&](auto e) {
-          hipLaunchKernelGGL((gemm_mfma_dma_kernel<true, LB_GEMM_NST, decltype(e)>), grid, dim3(256), 0, s, xp, rows, M, N, K,
-                             tiles_m, tiles_n, e);
-          return hipGetLastError();
-        });
-      return with_epi(epi, [&](auto e) {
-        hipLaunchKernelGGL((gemm_mfma_dma_kernel<false, LB_GEMM_NST, decltype(e)>), grid, dim3(256), 0, s, xp, rows, M, N, K,
-                           tiles_m, tiles_n, e);
-        return hipGetLastError();
-      });
-    }
-    if (p.big) {
-      const int tiles_m = ceil_div(M, 256);
-      const int tiles_n = ceil_div(N, dual ? 128 : 256);
-      dim3 grid(tiles_m * tiles_n);
-      if (dual)
-        return with_silu(epi, [&](auto e) {
-          hipLaunchKernelGGL((gemm_mfma8_kernel<true, decltype(e)>), grid, dim3(512), 0, s, xp, rows, M, N, K,
-                             tiles_m, tiles_n, e);
-          return hipGetLastError();
-        });
-      return with_epi(epi, [&](auto e) {
-        hipLaunchKernelGGL((gemm_mfma8_kernel<false, decltype(e)>), grid, dim3(512), 0, s, xp, rows, M, N, K,
                            tiles_m, tiles_n, e);
         return hipGetLastError();
       });

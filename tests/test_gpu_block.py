@@ -84,8 +84,11 @@ def small_bf16(**kw):
     return synth.workload("llama3_8b_gqa_prefill", **base)
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(n_kv=8), dict(seq=600, batch=1), dict(seq=33, n_kv=1)])
+@pytest.mark.parametrize("kw", [dict(), dict(n_kv=8), dict(seq=600, batch=1), dict(seq=33, n_kv=1),
+                                dict(n_q=6, n_kv=3, head_dim=16)])
 def test_small_block_bf16(kw):
+    """The last case (Q/K/V segments not on 32-row boundaries, head_dim 16)
+    takes the generic MFMA GEMM and the generic attention kernel."""
     inp = synth.make_block_inputs(small_bf16(**kw))
     y, _, _ = run_block(inp)
     check_bf16(f"small bf16 {kw}", y, inp)
