@@ -45,6 +45,10 @@ bool dtype_ok(int t) { return t == LLAMA_F32 || t == LLAMA_BF16; }
 
 size_t align_up(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
+// Up to this many token rows the QKV epilogue evaluates the RoPE angles
+// itself instead of reading a precomputed table.
+constexpr int64_t kRopeInlineRows = 256;
+
 // ---------------------------------------------------------------------------
 // kernel timing
 // ---------------------------------------------------------------------------
@@ -431,11 +435,17 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
     ep.kind = lb::EpiKind::Qkv; ep.out_dt = wdt;
     ep.q = q_buf; ep.k = k_buf; ep.v = v_buf; ep.positions = positions;
     ep.nq_hd = nq * hd; ep.nkv_hd = nkv * hd; ep.hd = hd; ep.seq_len = T; ep.kv_cap = kv_cap;
-    ep.rope_cs = rope_cs;
+    // Many tokens: the rotation angles' (cos, sin) are tabulated once per
+    // token and pair, then read by every GEMM tile; few tokens (decode): the
+    // epilogue evaluates them itself and the extra launch is skipped.
+    const bool table = M > kRopeInlineRows;
+    ep.rope_cs = table ? rope_cs : nullptr;
+    ep.rope = &rope;
     e = timed("qkv_rope", s, [&](const char** name) {
-      // the rotation angles' (cos, sin) per token and pair, then the GEMM
-      hipError_t er = lb::launch_rope_table(positions, M, hd, rope, wdt, rope_cs, s);
-      if (er != hipSuccess) return er;
+      if (table) {
+        hipError_t er = lb::launch_rope_table(positions, M, hd, rope, wdt, rope_cs, s);
+        if (er != hipSuccess) return er;
+      }
       return lb::launch_gemm(wdt, a_buf, M, d, wqkv, (nq + 2 * nkv) * hd, false, ep, gemm_ws, p.gemm, s, name);
     });
     if (e != hipSuccess) return hip_fail(e, "llama_block_forward: qkv projection");

@@ -782,10 +782,10 @@ hipError_t with_epi(const GemmEpi& e, F&& f) {
       if (e.out_dt == DType::F32)
         return f(EpiQkv<float>{static_cast<float*>(e.q), static_cast<float*>(e.k),
                                static_cast<float*>(e.v), e.positions, e.nq_hd, e.nkv_hd, e.hd,
-                               e.seq_len, e.kv_cap, e.rope_cs});
+                               e.seq_len, e.kv_cap, e.rope_cs, *e.rope});
       return f(EpiQkv<bf16_t>{static_cast<bf16_t*>(e.q), static_cast<bf16_t*>(e.k),
                               static_cast<bf16_t*>(e.v), e.positions, e.nq_hd, e.nkv_hd, e.hd,
-                              e.seq_len, e.kv_cap, e.rope_cs});
+                              e.seq_len, e.kv_cap, e.rope_cs, *e.rope});
     default:
       return hipErrorInvalidValue;
   }

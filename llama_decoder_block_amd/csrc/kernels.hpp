@@ -79,7 +79,9 @@ struct EpiQkv {
   T* v;
   const int32_t* positions;
   int nq_hd, nkv_hd, hd, seq_len, kv_cap;
-  const float* cs;  // [M, hd/2] (cos, sin) of each row's rotation angles (launch_rope_table)
+  const float* cs;  // [M, hd/2] (cos, sin) of each row's rotation angles (launch_rope_table),
+                    // or null: angles evaluated here from `rope` (few rows)
+  RopeTable rope;
 
   __device__ __forceinline__ T* dest(int m, int n, int pos) const {
     if (n < nq_hd) return q + static_cast<int64_t>(m) * nq_hd + n;
@@ -99,7 +101,16 @@ struct EpiQkv {
     if (cnt == 4 && (hd & 3) == 0) {
       // four columns (two pairs) in one head of one segment: one 4-wide store
       if (rot) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(angle(m, n));
+        f32x4 t;
+        if (cs) {
+          t = *reinterpret_cast<const f32x4*>(angle(m, n));
+        } else {
+          const int k = (n % hd) >> 1;
+          float s0, c0, s1, c1;
+          rope_sincos_t<T>(positions[m], rope.inv_freq[k], &s0, &c0);
+          rope_sincos_t<T>(positions[m], rope.inv_freq[k + 1], &s1, &c1);
+          t = f32x4{c0, s0, c1, s1};
+        }
         const float a0 = v[0] * t[0] - v[1] * t[1], b0 = v[0] * t[1] + v[1] * t[0];
         const float a1 = v[2] * t[2] - v[3] * t[3], b1 = v[2] * t[3] + v[3] * t[2];
         v[0] = a0; v[1] = b0; v[2] = a1; v[3] = b1;
@@ -110,7 +121,14 @@ struct EpiQkv {
     for (int pr = 0; pr + 1 < cnt; pr += 2) {
       float a = v[pr], b = v[pr + 1];
       if (rot) {
-        const f32x2 t = *reinterpret_cast<const f32x2*>(angle(m, n + pr));
+        f32x2 t;
+        if (cs)
+          t = *reinterpret_cast<const f32x2*>(angle(m, n + pr));
+        else {
+          float s0, c0;
+          rope_sincos_t<T>(positions[m], rope.inv_freq[((n + pr) % hd) >> 1], &s0, &c0);
+          t = f32x2{c0, s0};
+        }
         const float ra = a * t[0] - b * t[1];
         b = a * t[1] + b * t[0];
         a = ra;
@@ -172,7 +190,8 @@ struct GemmEpi {
   void* q; void* k; void* v;
   const int32_t* positions;
   int nq_hd, nkv_hd, hd, seq_len, kv_cap;
-  const float* rope_cs;  // [M, hd/2] (cos, sin) table from launch_rope_table
+  const float* rope_cs;  // [M, hd/2] (cos, sin) table from launch_rope_table, or null
+  const RopeTable* rope;  // the inverse frequencies (used when rope_cs is null)
 };
 
 // Workspace bytes the GEMM needs for a given problem (split-K partials).

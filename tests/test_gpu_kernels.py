@@ -311,6 +311,32 @@ def test_decode_attention_few_sequences_long_cache():
     assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, to64(v)))
 
 
+def test_decode_attention_long_context():
+    """One sequence at position 32768 against a 32769-slot cache (Llama-3-8B
+    heads): the split over workgroups with a merge through the workspace."""
+    B, S, nq, nkv, hd = 1, 32769, 32, 8, 128
+    q, k, v = attn_inputs(97, B, 1, S, nq, nkv, hd, "bf16")
+    pos = torch.tensor([[S - 1]], dtype=torch.int32)
+    out, used = decode_kernel_used(q, k, v, pos)
+    assert used == ["attention/attn_decode_splitk"]
+    ref = oracle.gqa_attention(to64(q), to64(k), to64(v), to64(pos).astype(np.int64))
+    report("decode 32K", out, ref)
+    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, to64(v)))
+
+
+def test_chunked_prefill_against_long_cache():
+    """A 256-token chunk at positions 7936..8191 attending an 8192-slot cache
+    (chunked prefill): flash kernel with positions, full and partial tiles."""
+    B, T, S, nq, nkv, hd = 1, 256, 8192, 32, 8, 128
+    q, k, v = attn_inputs(98, B, T, S, nq, nkv, hd, "bf16")
+    pos = (torch.arange(T, dtype=torch.int32) + (S - T)).reshape(1, T)
+    out = binding.gqa_attention(dev(q), dev(k), dev(v), dev(pos))
+    torch.cuda.synchronize()
+    ref = oracle.gqa_attention(to64(q), to64(k), to64(v), to64(pos).astype(np.int64))
+    report("chunked prefill", out, ref)
+    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, to64(v)))
+
+
 # ---------------------------------------------------------------------------
 # SwiGLU FFN (GEMMs: MFMA tiles, split-K path, VALU path)
 # ---------------------------------------------------------------------------
