@@ -262,8 +262,9 @@ gemm_mfma_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, in
 // check instead of being clamped.  Per K step kt each wavefront
 //   * issues the global loads of step kt+2 into one register staging set,
 //   * writes the staging set holding step kt+1 into the other LDS buffer,
-//   * runs 4 sub-steps of 16 MFMAs, reading the next sub-step's fragments
-//     after the first 4 MFMAs of the current one,
+//   * runs 4 sub-steps of 16 MFMAs with every memory instruction placed
+//     between two MFMAs: the loads and LDS stores between the first ones,
+//     the next sub-step's fragment reads one per MFMA after them,
 //   * and crosses the end-of-step barrier half-way through the last
 //     sub-step's MFMAs, then reads the first fragments of step kt+1.
 // Requires K % 64 == 0 and weight-segment boundaries at multiples of 32 rows.
@@ -350,14 +351,6 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
     for (int b = 0; b < TM; ++b)
       fb[f][b] = __builtin_bit_cast(bf16x8, lds[buf][BN * 8 + lds_idx(wave_m * WM + b * 32 + frag_row, ch)]);
   };
-  auto mfmas = [&](auto F, auto LO, auto HI) {
-    constexpr int f = decltype(F)::value;
-    constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
-#pragma unroll
-    for (int t = lo; t < hi; ++t)
-      acc[t / TM][t % TM] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][t / TM], fb[f][t % TM], acc[t / TM][t % TM], 0, 0, 0);
-  };
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
   auto barrier = [&]() {
     fence();
@@ -366,64 +359,78 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I4 = std::integral_constant<int, 4>;
-  using I8 = std::integral_constant<int, 8>;
-  using I16 = std::integral_constant<int, 16>;
 
-  // one K step on LDS buffer BUF; staging set P holds step kt+1, set Q
-  // receives step kt+2
+
+  // One K step on LDS buffer BUF; staging set P holds step kt+1, set Q
+  // receives step kt+2.  Every global load, LDS store and fragment read sits
+  // between two MFMAs, so the matrix core is never left waiting while a burst
+  // of memory instructions issues (4-5% faster than issuing them in groups).
+  // Straight-line on purpose: loads, stores and fragment reads are issued
+  // unconditionally (past the last K step the buffer range check returns
+  // zeros or in-bounds data that is never consumed), so the compiler can
+  // count outstanding loads exactly instead of waiting for the newest ones.
+  auto rd = [&](int bufi, int sub, auto F, int i) {
+    constexpr int f = decltype(F)::value;
+    const int ch = sub * 2 + frag_half;
+    if (i < TN)
+      fa[f][i] = __builtin_bit_cast(bf16x8, lds[bufi][lds_idx(wave_n * WN + i * 32 + frag_row, ch)]);
+    else
+      fb[f][i - TN] = __builtin_bit_cast(bf16x8, lds[bufi][BN * 8 + lds_idx(wave_m * WM + (i - TN) * 32 + frag_row, ch)]);
+  };
+  auto mf = [&](auto F, int t) {
+    constexpr int f = decltype(F)::value;
+    acc[t / TM][t % TM] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][t / TM], fb[f][t % TM], acc[t / TM][t % TM], 0, 0, 0);
+    fence();
+  };
   auto kstep = [&](int kt, auto BUFc, auto P, auto Q) {
     constexpr int buf = decltype(BUFc)::value;
-    // Straight-line on purpose: loads, stores and fragment reads are issued
-    // unconditionally (past the last K step the buffer range check returns
-    // zeros or in-bounds data that is never consumed), so the compiler can
-    // count outstanding loads exactly instead of waiting for the newest ones.
-    // sub-step 0
-    gload(kt + 2, 0, Q);
-    gload(kt + 2, 1, Q);
-    fence();
-    mfmas(I0{}, I0{}, I4{});
-    fence();
-    read_frags(buf, 1, I1{});
-    fence();
-    mfmas(I0{}, I4{}, I16{});
-    fence();
-    // sub-step 1
-    gload(kt + 2, 2, Q);
-    gload(kt + 2, 3, Q);
-    lstore(buf ^ 1, 0, P);
-    lstore(buf ^ 1, 1, P);
-    fence();
-    mfmas(I1{}, I0{}, I4{});
-    fence();
-    read_frags(buf, 2, I0{});
-    fence();
-    mfmas(I1{}, I4{}, I16{});
-    fence();
-    // sub-step 2
-    gload(kt + 2, 4, Q);
-    gload(kt + 2, 5, Q);
-    lstore(buf ^ 1, 2, P);
-    lstore(buf ^ 1, 3, P);
-    fence();
-    mfmas(I0{}, I0{}, I4{});
-    fence();
-    read_frags(buf, 3, I1{});
-    fence();
-    mfmas(I0{}, I4{}, I16{});
-    fence();
-    // sub-step 3, with the end-of-step barrier half-way
-    gload(kt + 2, 6, Q);
-    gload(kt + 2, 7, Q);
+    // sub-steps 0..2: memory operations between MFMAs 0..3, the next
+    // sub-step's fragment reads between MFMAs 4..11
+    auto sub = [&](auto F, auto NF, int s) {
+      if (s == 0) {
+        mf(F, 0); gload(kt + 2, 0, Q); fence();
+        mf(F, 1); gload(kt + 2, 1, Q); fence();
+        mf(F, 2); mf(F, 3);
+      } else {
+        const int ga = 2 * s, gs = 2 * (s - 1);
+        mf(F, 0); gload(kt + 2, ga, Q); fence();
+        mf(F, 1); gload(kt + 2, ga + 1, Q); fence();
+        mf(F, 2); lstore(buf ^ 1, gs, P); fence();
+        mf(F, 3); lstore(buf ^ 1, gs + 1, P); fence();
+      }
 #pragma unroll
-    for (int g = 4; g < GROUPS; ++g) lstore(buf ^ 1, g, P);
-    fence();
-    mfmas(I1{}, I0{}, I8{});
+      for (int i = 0; i < 8; ++i) {
+        mf(F, 4 + i);
+        rd(buf, s + 1, NF, i);
+        fence();
+      }
+#pragma unroll
+      for (int t = 12; t < 16; ++t) mf(F, t);
+    };
+    sub(I0{}, I1{}, 0);
+    sub(I1{}, I0{}, 1);
+    sub(I0{}, I1{}, 2);
+    // sub-step 3: loads and stores between MFMAs 0..7, the end-of-step
+    // barrier, then the next step's first fragments between MFMAs 8..11
+    mf(I1{}, 0); gload(kt + 2, 6, Q); fence();
+    mf(I1{}, 1); gload(kt + 2, 7, Q); fence();
+    mf(I1{}, 2); lstore(buf ^ 1, 4, P); fence();
+    mf(I1{}, 3); lstore(buf ^ 1, 5, P); fence();
+    mf(I1{}, 4); lstore(buf ^ 1, 6, P); fence();
+    mf(I1{}, 5); lstore(buf ^ 1, 7, P); fence();
+    mf(I1{}, 6);
+    mf(I1{}, 7);
     barrier();
-    read_frags(buf ^ 1, 0, I0{});
-    fence();
-    mfmas(I1{}, I8{}, I16{});
-    fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rd(buf ^ 1, 0, I0{}, 2 * i);
+      rd(buf ^ 1, 0, I0{}, 2 * i + 1);
+      fence();
+      mf(I1{}, 8 + i);
+    }
+#pragma unroll
+    for (int t = 12; t < 16; ++t) mf(I1{}, t);
   };
 
   // prologue: step 0 in LDS buffer 0 (staging set 0), step 1 in flight (set 1)
