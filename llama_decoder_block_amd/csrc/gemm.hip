@@ -451,6 +451,47 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
 
   // epilogue: register e of a 32x32 tile is feature row (e/4)*8 + half*4 + e%4
   // of the weight operand and token column lane%32
+  if constexpr (!DUAL) {
+    // Whole tile inside the output: the split epilogue.  Each lane's four
+    // token rows are resolved first, then the loads (or factors) of the next
+    // token row's 16 column groups are issued before the current row's
+    // results are stored, so every load overlaps other loads and stores.
+    if (m0 + BM <= M && out_n0 + BN <= N && epi.vec_ok()) {
+      typename Epi::Row rows[TM];
+#pragma unroll
+      for (int b = 0; b < TM; ++b) rows[b] = epi.row(m0 + wave_m * WM + b * 32 + frag_row);
+      f32x4 pre[2][TN * 4];
+      auto col = [&](int a, int j) { return out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4; };
+      auto issue = [&](int b) {
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pre[b & 1][a * 4 + j] = epi.pre(rows[b], col(a, j));
+      };
+      auto finish = [&](int b) {
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
+            epi.put(rows[b], col(a, j), pre[b & 1][a * 4 + j], v);
+          }
+      };
+      // (scheduling fences keep the accumulators in AGPRs until their row's
+      // turn, leaving VGPRs for the in-flight loads)
+      issue(0);
+#pragma unroll
+      for (int b = 0; b < TM; ++b) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (b + 1 < TM) issue(b + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(b);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int b = 0; b < TM; ++b) {
     const int m = m0 + wave_m * WM + b * 32 + frag_row;

@@ -31,6 +31,13 @@ struct WSeg {
 // hands each output row m four consecutive columns n..n+3 (n % 4 == 0,
 // `cnt` of them valid) to the epilogue.  For the fused gate/up product the
 // epilogue receives the gate and up accumulators of the same column c.
+//
+// The single-operand epilogues also offer a split form for whole groups of
+// four columns (when vec_ok()): row(m) gathers what depends on the row only,
+// pre(row, n) issues the group's loads (or computes its factors), and
+// put(row, n, pre, v) finishes and stores.  A tile epilogue issues pre() for
+// many groups before the first put(), so their loads are in flight together
+// instead of one load-use-store round trip per group.
 // ---------------------------------------------------------------------------
 
 // out[m, n] = acc (stored in TO)
@@ -38,6 +45,13 @@ template <typename TO>
 struct EpiStore {
   TO* out;
   int ldo;
+  using Row = int64_t;
+  __device__ __forceinline__ bool vec_ok() const { return (ldo & 3) == 0; }
+  __device__ __forceinline__ Row row(int m) const { return static_cast<int64_t>(m) * ldo; }
+  __device__ __forceinline__ f32x4 pre(Row, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ void put(Row r, int n, f32x4, const float v[4]) const {
+    Vec4<TO>::store(out + r + n, v);
+  }
   __device__ __forceinline__ void operator()(int m, int n, const float v[4], int cnt) const {
     TO* p = out + static_cast<int64_t>(m) * ldo + n;
     if (cnt == 4 && (ldo & 3) == 0) {
@@ -54,6 +68,20 @@ struct EpiResid {
   TR* out;
   const TR* resid;
   int ldo;
+  using Row = int64_t;
+  __device__ __forceinline__ bool vec_ok() const { return (ldo & 3) == 0; }
+  __device__ __forceinline__ Row row(int m) const { return static_cast<int64_t>(m) * ldo; }
+  __device__ __forceinline__ f32x4 pre(Row r, int n) const {
+    float t[4];
+    Vec4<TR>::load(resid + r + n, t);
+    return f32x4{t[0], t[1], t[2], t[3]};
+  }
+  __device__ __forceinline__ void put(Row r, int n, f32x4 res, const float v[4]) const {
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = res[i] + v[i];
+    Vec4<TR>::store(out + r + n, o);
+  }
   __device__ __forceinline__ void operator()(int m, int n, const float v[4], int cnt) const {
     const int64_t off = static_cast<int64_t>(m) * ldo + n;
     if (cnt == 4 && (ldo & 3) == 0) {
@@ -93,6 +121,51 @@ struct EpiQkv {
   }
   __device__ __forceinline__ const float* angle(int m, int n) const {
     return cs + (static_cast<int64_t>(m) * (hd >> 1) + ((n % hd) >> 1)) * 2;
+  }
+
+  // split form (whole groups of four columns inside one head of one segment)
+  struct Row {
+    int64_t m;       // token row
+    int64_t kv_row;  // row of k / v (cache slot row when kv_cap > 0)
+    int pos;         // rotation position
+  };
+  __device__ __forceinline__ bool vec_ok() const {
+    return (hd & 3) == 0 && (nq_hd & 3) == 0 && (nkv_hd & 3) == 0;
+  }
+  __device__ __forceinline__ Row row(int m) const {
+    Row r;
+    r.m = m;
+    r.pos = positions[m];
+    r.kv_row = kv_cap > 0 ? static_cast<int64_t>(m / seq_len) * kv_cap + r.pos : static_cast<int64_t>(m);
+    return r;
+  }
+  // (cos, sin) of the group's two pairs (unused for V columns)
+  __device__ __forceinline__ f32x4 pre(const Row& r, int n) const {
+    if (n >= nq_hd + nkv_hd) return f32x4{1.f, 0.f, 1.f, 0.f};
+    if (cs) return *reinterpret_cast<const f32x4*>(angle(static_cast<int>(r.m), n));
+    const int k = (n % hd) >> 1;
+    float s0, c0, s1, c1;
+    rope_sincos_t<T>(r.pos, rope.inv_freq[k], &s0, &c0);
+    rope_sincos_t<T>(r.pos, rope.inv_freq[k + 1], &s1, &c1);
+    return f32x4{c0, s0, c1, s1};
+  }
+  __device__ __forceinline__ void put(const Row& r, int n, f32x4 t, const float a[4]) const {
+    float o[4] = {a[0], a[1], a[2], a[3]};
+    T* d;
+    if (n < nq_hd) {
+      d = q + r.m * nq_hd + n;
+    } else {
+      const bool is_k = n < nq_hd + nkv_hd;
+      const int nn = is_k ? n - nq_hd : n - nq_hd - nkv_hd;
+      d = (is_k ? k : v) + r.kv_row * nkv_hd + nn;
+    }
+    if (n < nq_hd + nkv_hd) {
+      o[0] = a[0] * t[0] - a[1] * t[1];
+      o[1] = a[0] * t[1] + a[1] * t[0];
+      o[2] = a[2] * t[2] - a[3] * t[3];
+      o[3] = a[2] * t[3] + a[3] * t[2];
+    }
+    Vec4<T>::store(d, o);
   }
   __device__ __forceinline__ void operator()(int m, int n, const float v4[4], int cnt) const {
     const int pos = kv_cap > 0 ? positions[m] : 0;
