@@ -179,8 +179,7 @@ def main():
                          "reference reading for scaling the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md on sharding); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -608,11 +608,40 @@ splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t split_s
   const int n = static_cast<int>(gid - static_cast<int64_t>(m) * groups) * 4;
   const int cnt = min(4, N - n);
   float v[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int z = 0; z < splits; ++z) {
-    const float* p = part + z * split_stride + static_cast<int64_t>(m) * ldp + n;
-    for (int i = 0; i < cnt; ++i) {
-      v[i] += p[i];
-      if constexpr (DUAL) u[i] += p[N + i];
+  const float* p0 = part + static_cast<int64_t>(m) * ldp + n;
+  if (cnt == 4 && (ldp & 3) == 0 && (N & 3) == 0 && (split_stride & 3) == 0) {
+    // whole 16-byte groups: all splits' loads issued before the sums
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
+    int z = 0;
+    for (; z + 4 <= splits; z += 4) {
+      f32x4 t[4], tu[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        t[i] = *reinterpret_cast<const f32x4*>(p0 + (z + i) * split_stride);
+        if constexpr (DUAL) tu[i] = *reinterpret_cast<const f32x4*>(p0 + (z + i) * split_stride + N);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a += t[i];
+        if constexpr (DUAL) c += tu[i];
+      }
+    }
+    for (; z < splits; ++z) {
+      a += *reinterpret_cast<const f32x4*>(p0 + z * split_stride);
+      if constexpr (DUAL) c += *reinterpret_cast<const f32x4*>(p0 + z * split_stride + N);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      u[i] = c[i];
+    }
+  } else {
+    for (int z = 0; z < splits; ++z) {
+      const float* p = p0 + z * split_stride;
+      for (int i = 0; i < cnt; ++i) {
+        v[i] += p[i];
+        if constexpr (DUAL) u[i] += p[N + i];
+      }
     }
   }
   if constexpr (DUAL)

@@ -1,6 +1,6 @@
 """Block-level parity of llama_block_forward against the CPU oracle (needs a GPU).
 
-Gates (the readings of the stated tolerances, derived in the design doc):
+Gates (the readings of the stated tolerances):
   * fp32 path: max relative error (floored at 1e-3 of the tensor's max) <= 1e-4;
   * bf16 path: relative Frobenius error <= 1e-2 against the exact fp64 oracle,
     and max abs error <= 5e-2 against the bf16 storage-point oracle, on the
