@@ -18,6 +18,10 @@ states.  Pages cited (by title, section and equation; no line numbers):
   [MA] "LLaMA Architecture > Model Architecture"
        (mbrenndoerfer.com/writing/llama-architecture-design-training-efficiency/model-architecture)
 
+The 8-bit KV-cache model (``oracle.fp8``: E4M3 codes with one fp32 scale per
+cache row) is pinned against the format definition in
+``tests/test_oracle_fp8_pins.py``.
+
 Parity status: every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_pins.py`` (closed forms, the [L3] worked example,
 invariants, library special cases and brute force).  The bf16 storage-point
@@ -40,4 +44,5 @@ from .reference import (  # noqa: F401
     decode_step,
 )
 from .bf16 import round_bf16  # noqa: F401
+from . import fp8  # noqa: F401
 from . import bruteforce  # noqa: F401

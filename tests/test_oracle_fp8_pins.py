@@ -1,0 +1,114 @@
+"""Pins of the oracle's 8-bit KV-cache model (oracle/fp8.py) against the
+E4M3 format definition and the scale convention it states ([LA]
+"Troubleshooting Common Deployment Faults", item 3, names the 8-bit cache;
+the format and scale are readings).  Nothing here uses a GPU."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fp8
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def test_decode_known_codes():
+    # values fixed by the format: bias 7, 3 mantissa bits, subnormal spacing 2**-9
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5,
+             0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in table.items():
+        assert fp8.e4m3_decode(np.uint8(c)) == v, hex(c)
+    assert np.signbit(fp8.e4m3_decode(np.uint8(0x80)))
+    assert np.isnan(fp8.e4m3_decode(np.uint8(0x7F))) and np.isnan(fp8.e4m3_decode(np.uint8(0xFF)))
+
+
+def test_decode_grid_is_strictly_increasing_with_126_positive_values():
+    pos = fp8.e4m3_decode(np.arange(0x01, 0x7F, dtype=np.uint8))
+    assert len(pos) == 126
+    assert np.all(np.diff(pos) > 0)
+    # spacing doubles at each binade boundary: 2**-9 up to 2**-5, then 2**(e-3)
+    assert np.all(np.diff(fp8.e4m3_decode(np.arange(0x00, 0x10, dtype=np.uint8))) == 2.0 ** -9)
+    assert fp8.e4m3_decode(np.uint8(0x7E)) - fp8.e4m3_decode(np.uint8(0x7D)) == 32.0
+
+
+def test_encode_decode_round_trip_all_codes():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(fp8.e4m3_encode(fp8.e4m3_decode(codes)), codes)
+
+
+def test_ties_go_to_even_mantissa():
+    c = np.arange(0x00, 0x7E)
+    mids = 0.5 * (fp8.e4m3_decode(c) + fp8.e4m3_decode(c + 1))
+    want = np.where(c % 2 == 0, c, c + 1)
+    assert np.array_equal(fp8.e4m3_encode(mids), want)
+    assert np.array_equal(fp8.e4m3_encode(-mids), want | 0x80)
+
+
+def test_nearest_rounding_bruteforce():
+    grid = fp8.e4m3_decode(np.arange(0x00, 0x7F, dtype=np.uint8))
+    x = np.concatenate([rng(1).uniform(0, 448, 4000), rng(2).uniform(0, 0.05, 4000)])
+    got = fp8.e4m3_decode(fp8.e4m3_encode(x))
+    dist = np.abs(x[:, None] - grid[None, :])
+    best = dist.min(axis=1)
+    assert np.all(np.abs(got - x) == best)
+
+
+def test_saturation_sign_and_nan():
+    enc = fp8.e4m3_encode(np.array([448.0, 463.9, 1e30, -1e30, -0.0, 2.0 ** -11, -(2.0 ** -11), np.nan]))
+    assert list(enc) == [0x7E, 0x7E, 0x7E, 0xFE, 0x80, 0x00, 0x80, 0x7F]
+
+
+def test_quantize_rows_scale_and_extreme_code():
+    x = rng(3).standard_normal((16, 128)).astype(np.float32).astype(np.float64)
+    codes, s = fp8.quantize_rows(x)
+    assert s.dtype == np.float32
+    assert np.array_equal(s, (np.max(np.abs(x), axis=1).astype(np.float32) / np.float32(448)).astype(np.float32))
+    # the largest magnitude of every row lands on +-448
+    i = np.argmax(np.abs(x), axis=1)
+    ext = codes[np.arange(16), i]
+    assert np.all((ext & 0x7F) == 0x7E)
+
+
+def test_quantize_rows_error_bound():
+    x = (rng(4).standard_normal((64, 128)) * np.exp(rng(5).uniform(-6, 6, (64, 1)))).astype(np.float32)
+    x = x.astype(np.float64)
+    codes, s = fp8.quantize_rows(x)
+    xh = fp8.dequantize_rows(codes, s)
+    # half a step of the 3-bit mantissa, or half a subnormal step, in units of s
+    # (plus the fp32 rounding of x / s)
+    bound = np.abs(x) * (2.0 ** -4 + 2.0 ** -22) + s[:, None].astype(np.float64) * 2.0 ** -10
+    assert np.all(np.abs(xh - x) <= bound)
+
+
+def test_zero_row_stores_zero_scale_and_codes():
+    x = np.zeros((2, 128))
+    x[1, 5] = -0.0
+    codes, s = fp8.quantize_rows(x)
+    assert np.all(s == 0) and np.all(codes == 0)
+
+
+def test_grid_values_with_unit_scale_are_stored_exactly():
+    # rows whose maximum is 448 and whose values lie on the E4M3 grid: s = 1 and
+    # the cache holds exactly the input, so attention over it is the plain one
+    g = rng(6)
+    grid = fp8.e4m3_decode(np.arange(0x00, 0x7F, dtype=np.uint8))
+    k = g.choice(grid, size=(1, 9, 2, 128)) * g.choice([-1.0, 1.0], size=(1, 9, 2, 128))
+    v = g.choice(grid, size=(1, 9, 2, 128)) * g.choice([-1.0, 1.0], size=(1, 9, 2, 128))
+    k[..., 0] = 448.0
+    v[..., 3] = -448.0
+    kc, vc, ks, vs = fp8.kv_cache_from_rows(k, v)
+    assert ks.shape == (1, 2, 9) and np.all(ks == 1.0) and np.all(vs == 1.0)
+    assert np.array_equal(fp8.kv_cache_values(kc, ks), k)
+    assert np.array_equal(fp8.kv_cache_values(vc, vs), v)
+    q = g.standard_normal((1, 1, 4, 128)) * 0.01
+    vis = np.array([[8]])
+    a = oracle.gqa_attention(q, fp8.kv_cache_values(kc, ks), fp8.kv_cache_values(vc, vs), vis)
+    b = oracle.gqa_attention(q, k, v, vis)
+    assert np.array_equal(a, b)
+
+
+def test_rejects_values_fp32_cannot_hold():
+    with pytest.raises(ValueError):
+        fp8.quantize_rows(np.array([[1.0 + 2.0 ** -40]]))
