@@ -165,6 +165,65 @@ def cpu_baseline(tokens):
                       f"tokens of the Llama-3-8B prefill (same seeded inputs), one pass, {dt:.1f} s"}
 
 
+def bench_decode_fp8kv(wd, dev, args):
+    """The decode workload against an 8-bit KV cache (E4M3 codes + one fp32
+    scale per row) holding the same synthetic history, quantized on the GPU by
+    the library's cache writer; timed like the bf16 decode step."""
+    inp = synth.make_block_inputs(wd)
+    w = {k: v.to(dev) for k, v in inp.weights.items()}
+    x = inp.x.to(dev)
+    pos = inp.positions.to(dev).reshape(-1)
+    B, cap, nkv, hd = wd.batch, wd.kv_cap, wd.n_kv, wd.head_dim
+    k8, v8, ks, vs = binding.fp8_cache(B, cap, nkv, hd, dev)
+    hist = torch.arange(wd.decode_pos, dtype=torch.int32, device=dev).repeat(B, 1)
+    kc, vc = inp.k_cache.to(dev), inp.v_cache.to(dev)
+    binding.kv_append_fp8(kc[:, :wd.decode_pos].contiguous(), vc[:, :wd.decode_pos].contiguous(), hist,
+                          k8, v8, ks, vs)
+    del kc, vc
+    need = binding.block_fp8kv_workspace_bytes(B, wd.d_model, wd.n_q, nkv, hd, wd.d_ff, cap, binding.F32)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+
+    def step():
+        binding.block_forward_fp8kv(x, w, pos, wd.n_q, nkv, wd.theta, wd.eps, k8, v8, ks, vs, y=y, workspace=ws)
+    scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    dms, _, dk = time_steps(step, args.decode_steps, args.warmup, flush=lambda: scratch.sum())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    gms, gper, _ = time_steps(graph.replay, args.decode_steps, args.warmup, flush=lambda: scratch.sum())
+    del scratch, graph
+    shd = shape_of(wd)
+    attend = wd.decode_pos + 1
+    dwork = wm.step_work(shd, B, 1, attend_len=attend, kv_bytes=wm.FP8KV_BYTES_PER_ELEM)
+    table = kernel_table(dk, dwork)
+    name = DECODE_ATTN + "_fp8kv"
+    n_at, ms_at = dk.get(name, (0, 0.0))
+    at_avg = ms_at / max(n_at, 1)
+    at_bytes = dwork["attention"][1]
+    at_gbs = at_bytes / (at_avg * 1e-3) / 1e9 if n_at else 0.0
+    log(f"[bench] decode, 8-bit KV cache: {gms * 1e3:.1f} us/step in a graph (median "
+        f"{gper[len(gper) // 2] * 1e3:.1f}); eager {dms * 1e3:.1f} us/step; attention {at_avg * 1e3:.1f} us = "
+        f"{at_gbs:.0f} GB/s")
+    for k, row in table.items():
+        log(f"[bench]   {k:40s} {row}")
+    out = {
+        "workload": f"{DECODE} with an 8-bit KV cache (E4M3 codes [{B},{nkv},{cap},{hd}] + fp32 row scales "
+                    f"[{B},{nkv},{cap}]), same history quantized on the GPU, last-level cache flushed between steps",
+        "ms_per_step": round(gms, 4),
+        "ms_median": round(gper[len(gper) // 2], 4),
+        "tokens_per_s": round(B / (gms * 1e-3), 1),
+        "eager_ms_per_step": round(dms, 4),
+        "attention": {"kernel": name, "bound": "hbm", "avg_us": round(at_avg * 1e3, 2), "bytes": at_bytes,
+                      "achieved": round(at_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(at_gbs / HBM_PEAK_GBS, 4)},
+        "kernels": table,
+    }
+    del step, w, x, k8, v8, ks, vs, ws, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +329,7 @@ def main():
             log(f"[bench]   {k:40s} {row}")
         del dstep
         torch.cuda.empty_cache()
+        decode["fp8kv"] = bench_decode_fp8kv(wd, dev, args)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define LLAMA_BLOCK_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define LLAMA_BLOCK_VERSION 10100 /* major*10000 + minor*100 + patch */
 
 enum llama_dtype { LLAMA_F32 = 0, LLAMA_BF16 = 1 };
 
@@ -161,6 +161,65 @@ size_t llama_block_forward_workspace_bytes(int32_t batch, int32_t seq_len, int32
                                            int32_t n_q_heads, int32_t n_kv_heads,
                                            int32_t head_dim, int32_t d_ff, int32_t kv_cap,
                                            int wdtype, int rdtype);
+
+/* 8-bit KV cache ([LA] "Troubleshooting Common Deployment Faults", item 3:
+ * an 8-bit KV cache halves the bytes_per_elem factor of the KV-cache memory
+ * formula in [LA] §4).  The pages fix no format or scale; this library uses
+ * OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities, largest finite 448, 0x7F/0xFF are NaN and never written) with
+ * one fp32 scale per cached row of head_dim values:
+ *   s = max_i |x_i| / 448 (fp32 division);
+ *   code_i = x_i / s (fp32 division) rounded to the nearest E4M3 value, ties
+ *            to the even mantissa, magnitudes beyond 448 clamped, sign kept;
+ *   a row whose maximum is 0 stores s = 0 and all-zero codes;
+ *   the cached value is s * E4M3(code_i).
+ * Layouts: codes k_cache, v_cache [batch, n_kv, kv_cap, hd] (one byte each:
+ * unlike the bf16 caches, the slots of one KV head are contiguous, so the
+ * decode kernel streams each head's history as one block); scales k_scale,
+ * v_scale [batch, n_kv, kv_cap] fp32.  Slots never written
+ * hold arbitrary bytes and are never read (a query at position p reads slots
+ * 0..p only). */
+
+/* Quantizes the rows k, v [batch, seq_len, n_kv, hd] (wdtype; NaN inputs are
+ * not supported) and stores codes and scales at slot positions[b, t] of
+ * sequence b.  Tokens whose slot is outside [0, kv_cap) are skipped on the
+ * device (no write).  head_dim must be 64, 128 or 256. */
+int llama_kv_append_fp8(const void* k, const void* v, const int32_t* positions, int32_t batch,
+                        int32_t seq_len, int32_t n_kv_heads, int32_t head_dim, int wdtype,
+                        void* k_cache, void* v_cache, float* k_scale, float* v_scale, int32_t kv_cap,
+                        void* stream);
+
+/* Decode attention over an 8-bit cache: one query token per sequence,
+ * otherwise the operation of llama_gqa_attention with q_len == 1.  Scores are
+ * k_scale[slot] * (q . E4M3(codes)) / sqrt(hd); the weights multiply
+ * v_scale[slot] * E4M3(codes).  q, out: bf16 [batch, n_q, hd]; positions:
+ * [batch] (query b sees slots 0..positions[b], each < kv_cap).  head_dim must
+ * be 128 and n_q/n_kv one of 1, 2, 4, 8.  workspace: at least
+ * llama_gqa_attention_fp8kv_workspace_bytes(...) bytes. */
+int llama_gqa_attention_fp8kv(const void* q, const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale, void* out,
+                              const int32_t* positions, int32_t batch, int32_t kv_cap,
+                              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                              void* workspace, size_t ws_bytes, void* stream);
+size_t llama_gqa_attention_fp8kv_workspace_bytes(int32_t batch, int32_t kv_cap, int32_t n_q_heads,
+                                                 int32_t n_kv_heads, int32_t head_dim);
+
+/* The decode step of llama_block_forward (seq_len == 1, bf16 weights and
+ * operands, residual stream in rdtype) against an 8-bit cache: the new
+ * token's rotated k and its v are quantized into slot positions[b] (as
+ * llama_kv_append_fp8 does), then query b attends slots 0..positions[b]
+ * through llama_gqa_attention_fp8kv's kernel.  x, y: [batch, 1, d_model];
+ * positions: [batch].  workspace: at least
+ * llama_block_forward_fp8kv_workspace_bytes(...) bytes. */
+int llama_block_forward_fp8kv(const void* x, void* y, const llama_block_weights* w,
+                              const int32_t* positions, void* k_cache, void* v_cache,
+                              float* k_scale, float* v_scale, int32_t kv_cap, int32_t batch,
+                              int32_t d_model, int32_t n_q_heads, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t d_ff, double rope_theta, double eps,
+                              int rdtype, void* workspace, size_t ws_bytes, void* stream);
+size_t llama_block_forward_fp8kv_workspace_bytes(int32_t batch, int32_t d_model, int32_t n_q_heads,
+                                                 int32_t n_kv_heads, int32_t head_dim, int32_t d_ff,
+                                                 int32_t kv_cap, int rdtype);
 
 /* Host-only helpers. */
 const char* llama_last_error(void);    /* thread-local text of the last failure ("" if none) */

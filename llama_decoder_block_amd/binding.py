@@ -22,7 +22,9 @@ FUNCTIONS = [
     "llama_swiglu_ffn", "llama_swiglu_ffn_workspace_bytes", "llama_block_forward",
     "llama_block_forward_workspace_bytes", "llama_last_error", "llama_status_string",
     "llama_version", "llama_profile_enable", "llama_profile_reset", "llama_profile_collect",
-    "llama_profile_query", "llama_profile_names",
+    "llama_profile_query", "llama_profile_names", "llama_kv_append_fp8", "llama_gqa_attention_fp8kv",
+    "llama_gqa_attention_fp8kv_workspace_bytes", "llama_block_forward_fp8kv",
+    "llama_block_forward_fp8kv_workspace_bytes",
 ]
 
 
@@ -74,6 +76,15 @@ def lib():
         "llama_profile_collect": ([], _int),
         "llama_profile_query": ([ctypes.c_char_p, ctypes.POINTER(_i64), ctypes.POINTER(_f64)], _int),
         "llama_profile_names": ([ctypes.c_char_p, _sz], _int),
+        "llama_kv_append_fp8": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _int, _vp, _vp, _vp, _vp, _i32, _vp],
+                                _int),
+        "llama_gqa_attention_fp8kv": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
+                                       _sz, _vp], _int),
+        "llama_gqa_attention_fp8kv_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32], _sz),
+        "llama_block_forward_fp8kv": ([_vp, _vp, ctypes.POINTER(BlockWeights), _vp, _vp, _vp, _vp, _vp, _i32,
+                                       _i32, _i32, _i32, _i32, _i32, _i32, _f64, _f64, _int, _vp, _sz, _vp],
+                                      _int),
+        "llama_block_forward_fp8kv_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _int], _sz),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -97,7 +108,12 @@ def _dt(t):
 
 
 def _p(t):
-    return None if t is None else t.data_ptr()
+    """Device pointer of a dense row-major tensor (the layouts the library reads)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError(f"tensor of shape {tuple(t.shape)} is not contiguous")
+    return t.data_ptr()
 
 
 def _stream():
@@ -192,6 +208,62 @@ def block_forward(x, w, positions, n_q_heads, n_kv_heads, rope_theta, eps, k_cac
                                  kv_cap, B, T, d, n_q_heads, n_kv_heads, hd, dff, rope_theta, eps, wdt, rdt,
                                  _p(ws), nbytes, _stream()))
     return y
+
+
+# --- 8-bit KV cache -----------------------------------------------------------
+def fp8_cache(batch, kv_cap, n_kv, hd, device):
+    """Empty 8-bit cache: (k codes, v codes) uint8 [B, n_kv, kv_cap, hd] and
+    (k scales, v scales) fp32 [B, n_kv, kv_cap]."""
+    k8 = torch.zeros(batch, n_kv, kv_cap, hd, dtype=torch.uint8, device=device)
+    v8 = torch.zeros_like(k8)
+    ks = torch.zeros(batch, n_kv, kv_cap, dtype=torch.float32, device=device)
+    vs = torch.zeros_like(ks)
+    return k8, v8, ks, vs
+
+
+def kv_append_fp8(k, v, positions, k8, v8, ks, vs):
+    """Quantize k, v [B, T, n_kv, hd] into the 8-bit cache at slots positions [B, T]."""
+    B, T, nkv, hd = k.shape
+    _check(lib().llama_kv_append_fp8(_p(k), _p(v), _p(positions), B, T, nkv, hd, _dt(k), _p(k8), _p(v8),
+                                     _p(ks), _p(vs), k8.shape[2], _stream()))
+
+
+def gqa_attention_fp8kv(q, k8, v8, ks, vs, positions, out=None, workspace=None):
+    """Decode attention: q [B, 1, n_q, hd] bf16 (or [B, n_q, hd]); 8-bit cache;
+    positions [B] int32."""
+    B, nq, hd = q.shape[0], q.shape[-2], q.shape[-1]
+    nkv, kv_cap = k8.shape[1], k8.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    L = lib()
+    need = L.llama_gqa_attention_fp8kv_workspace_bytes(B, kv_cap, nq, nkv, hd)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check(L.llama_gqa_attention_fp8kv(_p(q), _p(k8), _p(v8), _p(ks), _p(vs), _p(out), _p(positions), B, kv_cap,
+                                       nq, nkv, hd, _p(ws), nbytes, _stream()))
+    return out
+
+
+def block_forward_fp8kv(x, w, positions, n_q_heads, n_kv_heads, rope_theta, eps, k8, v8, ks, vs, y=None,
+                        workspace=None):
+    """Decode step x [B, 1, d] against the 8-bit cache (updated in place)."""
+    B, T, d = x.shape
+    hd = w["wq"].shape[0] // n_q_heads
+    dff = w["w_gate"].shape[0]
+    kv_cap = k8.shape[2]
+    if y is None:
+        y = torch.empty_like(x)
+    L = lib()
+    need = L.llama_block_forward_fp8kv_workspace_bytes(B, d, n_q_heads, n_kv_heads, hd, dff, kv_cap, _dt(x))
+    ws, nbytes = _workspace(need, x.device, workspace)
+    wt = make_weights(w)
+    _check(L.llama_block_forward_fp8kv(_p(x), _p(y), ctypes.byref(wt), _p(positions), _p(k8), _p(v8), _p(ks),
+                                       _p(vs), kv_cap, B, d, n_q_heads, n_kv_heads, hd, dff, rope_theta, eps,
+                                       _dt(x), _p(ws), nbytes, _stream()))
+    return y
+
+
+def block_fp8kv_workspace_bytes(batch, d, nq, nkv, hd, dff, kv_cap, rdtype):
+    return lib().llama_block_forward_fp8kv_workspace_bytes(batch, d, nq, nkv, hd, dff, kv_cap, rdtype)
 
 
 # --- kernel timing -----------------------------------------------------------

@@ -324,20 +324,23 @@ struct BlockPlan {
   size_t a, q, k, v, o, h, mact, attn, gemm, cs, total;
 };
 
+// fp8: the cache is 8-bit, so the new tokens' k and v go to workspace rows
+// first and are quantized into the cache by a separate pass.
 BlockPlan block_plan(int B, int T, int d, int nq, int nkv, int hd, int dff, int kv_cap, DType wdt,
-                     DType rdt) {
+                     DType rdt, bool fp8 = false) {
   const size_t M = static_cast<size_t>(B) * T;
   const size_t wb = lb::dtype_bytes(wdt), rb = lb::dtype_bytes(rdt);
   BlockPlan p{};
   p.a = align_up(M * d * wb);  // also holds f (the FFN pre-norm output)
   p.q = align_up(M * nq * hd * wb);
-  p.k = kv_cap > 0 ? 0 : align_up(M * nkv * hd * wb);
+  p.k = kv_cap > 0 && !fp8 ? 0 : align_up(M * nkv * hd * wb);
   p.v = p.k;
   p.o = align_up(M * nq * hd * wb);
   p.h = align_up(M * d * rb);
   p.mact = align_up(M * dff * wb);
   const int S = kv_cap > 0 ? kv_cap : T;
-  p.attn = align_up(lb::attention_workspace_bytes(wdt, B, T, S, nq, nkv, hd));
+  p.attn = align_up(fp8 ? lb::attention_fp8kv_workspace_bytes(B, S, nq, nkv)
+                        : lb::attention_workspace_bytes(wdt, B, T, S, nq, nkv, hd));
   size_t g = lb::gemm_workspace_bytes(wdt, static_cast<int>(M), (nq + 2 * nkv) * hd, d, false);
   g = std::max(g, lb::gemm_workspace_bytes(wdt, static_cast<int>(M), d, nq * hd, false));
   g = std::max(g, lb::gemm_workspace_bytes(wdt, static_cast<int>(M), dff, d, true));
@@ -362,14 +365,20 @@ size_t llama_block_forward_workspace_bytes(int32_t batch, int32_t seq_len, int32
       .total;
 }
 
-int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
-                        const int32_t* positions, void* k_cache, void* v_cache, int32_t kv_cap,
-                        int32_t batch, int32_t seq_len, int32_t d_model, int32_t n_q_heads,
-                        int32_t n_kv_heads, int32_t head_dim, int32_t d_ff, double rope_theta,
-                        double eps, int wdtype, int rdtype, void* workspace, size_t ws_bytes,
-                        void* stream) {
-  if (!dtype_ok(wdtype) || !dtype_ok(rdtype))
-    return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code (wdtype=%d rdtype=%d)", wdtype, rdtype);
+namespace {
+
+// 8-bit cache of llama_block_forward_fp8kv
+struct Fp8Cache {
+  void* k8;
+  void* v8;
+  float* k_scale;
+  float* v_scale;
+};
+
+// Validation shared by llama_block_forward and llama_block_forward_fp8kv.
+int check_block_args(const void* x, void* y, const llama_block_weights* w, const int32_t* positions,
+                     int32_t batch, int32_t seq_len, int32_t d_model, int32_t n_q_heads, int32_t n_kv_heads,
+                     int32_t head_dim, int32_t d_ff, double rope_theta, double eps, int32_t kv_cap) {
   if (batch < 0 || seq_len < 0 || d_model <= 0 || d_ff <= 0)
     return fail(LLAMA_ERR_INVALID_ARGUMENT, "batch, seq_len must be >= 0; d_model, d_ff > 0");
   int st = check_heads(n_q_heads, n_kv_heads, head_dim);
@@ -377,27 +386,32 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
   if (!(rope_theta > 0.0)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "rope_theta must be > 0");
   if (!(eps >= 0.0)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "eps must be >= 0");
   if (kv_cap < 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "kv_cap must be >= 0");
-  const bool has_cache = kv_cap > 0;
-  if (has_cache != (k_cache != nullptr) || has_cache != (v_cache != nullptr))
-    return fail(LLAMA_ERR_INVALID_ARGUMENT, "k_cache and v_cache must both be given exactly when kv_cap > 0");
   if (static_cast<int64_t>(batch) * seq_len > 0x7fffffff)
     return fail(LLAMA_ERR_UNSUPPORTED, "batch*seq_len too large");
-  if (batch == 0 || seq_len == 0) return ok();
+  if (batch == 0 || seq_len == 0) return LLAMA_OK;
   if (!x || !y || !w || !positions)
     return fail(LLAMA_ERR_INVALID_ARGUMENT, "x, y, weights and positions must be non-null");
   if (!w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->ffn_norm || !w->w_gate || !w->w_up ||
       !w->w_down)
     return fail(LLAMA_ERR_INVALID_ARGUMENT, "every weight pointer must be non-null");
   if (y == x) return fail(LLAMA_ERR_INVALID_ARGUMENT, "y must not alias x");
-  for (const void* p : std::initializer_list<const void*>{x, static_cast<const void*>(y), w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->ffn_norm,
-                        w->w_gate, w->w_up, w->w_down, static_cast<const void*>(k_cache),
-                        static_cast<const void*>(v_cache), workspace})
-    if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  for (const void* p : std::initializer_list<const void*>{x, static_cast<const void*>(y), w->attn_norm, w->wq, w->wk,
+                                                          w->wv, w->wo, w->ffn_norm, w->w_gate, w->w_up, w->w_down})
+    if (!aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  return LLAMA_OK;
+}
 
-  const DType wdt = static_cast<DType>(wdtype), rdt = static_cast<DType>(rdtype);
-  const int B = batch, T = seq_len, d = d_model, nq = n_q_heads, nkv = n_kv_heads, hd = head_dim;
+// The block's launch sequence (arguments already validated).  With c8 the
+// cache is 8-bit: the Q/K/V epilogue stores this call's k and v rows in the
+// workspace, kv_append_fp8 quantizes them into the cache and the decode
+// attention reads the codes and scales.
+int run_block(const void* x, void* y, const llama_block_weights* w, const int32_t* positions, void* k_cache,
+              void* v_cache, int32_t kv_cap, int B, int T, int d, int nq, int nkv, int hd, int d_ff,
+              double rope_theta, double eps, DType wdt, DType rdt, void* workspace, size_t ws_bytes,
+              hipStream_t s, const Fp8Cache* c8) {
+  const bool has_cache = kv_cap > 0;
   const int M = B * T;
-  const BlockPlan p = block_plan(B, T, d, nq, nkv, hd, d_ff, kv_cap, wdt, rdt);
+  const BlockPlan p = block_plan(B, T, d, nq, nkv, hd, d_ff, kv_cap, wdt, rdt, c8 != nullptr);
   if (ws_bytes < p.total || !workspace)
     return fail(LLAMA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total, ws_bytes);
 
@@ -405,15 +419,14 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
   auto carve = [&](size_t n) { uint8_t* r = cur; cur += n; return r; };
   void* a_buf = carve(p.a);
   void* q_buf = carve(p.q);
-  void* k_buf = has_cache ? k_cache : carve(p.k);
-  void* v_buf = has_cache ? v_cache : carve(p.v);
+  void* k_buf = has_cache && !c8 ? k_cache : carve(p.k);
+  void* v_buf = has_cache && !c8 ? v_cache : carve(p.v);
   void* o_buf = carve(p.o);
   void* h_buf = carve(p.h);
   void* mact = carve(p.mact);
   void* attn_ws = carve(p.attn);
   void* gemm_ws = carve(p.gemm);
   float* rope_cs = reinterpret_cast<float*>(carve(p.cs));
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const lb::RopeTable rope = make_rope(hd, rope_theta);
   const float feps = static_cast<float>(eps);
   hipError_t e;
@@ -423,7 +436,7 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
     *name = "rmsnorm";
     return lb::launch_rmsnorm(x, nullptr, w->attn_norm, a_buf, nullptr, M, d, feps, wdt, rdt, s);
   });
-  if (e != hipSuccess) return hip_fail(e, "llama_block_forward: attention norm");
+  if (e != hipSuccess) return hip_fail(e, "block forward: attention norm");
 
   // a2-a4: fused Q/K/V projection with RoPE and (cache) stores
   {
@@ -434,7 +447,7 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
     lb::GemmEpi ep{};
     ep.kind = lb::EpiKind::Qkv; ep.out_dt = wdt;
     ep.q = q_buf; ep.k = k_buf; ep.v = v_buf; ep.positions = positions;
-    ep.nq_hd = nq * hd; ep.nkv_hd = nkv * hd; ep.hd = hd; ep.seq_len = T; ep.kv_cap = kv_cap;
+    ep.nq_hd = nq * hd; ep.nkv_hd = nkv * hd; ep.hd = hd; ep.seq_len = T; ep.kv_cap = c8 ? 0 : kv_cap;
     // Many tokens: the rotation angles' (cos, sin) are tabulated once per
     // token and pair, then read by every GEMM tile; few tokens (decode): the
     // epilogue evaluates them itself and the extra launch is skipped.
@@ -448,20 +461,33 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
       }
       return lb::launch_gemm(wdt, a_buf, M, d, wqkv, (nq + 2 * nkv) * hd, false, ep, gemm_ws, p.gemm, s, name);
     });
-    if (e != hipSuccess) return hip_fail(e, "llama_block_forward: qkv projection");
+    if (e != hipSuccess) return hip_fail(e, "block forward: qkv projection");
+  }
+  if (c8) {
+    e = timed("kv_append_fp8", s, [&](const char** name) {
+      *name = "kv_append_fp8";
+      return lb::launch_kv_append_fp8(k_buf, v_buf, positions, M, T, nkv, hd, wdt, c8->k8, c8->v8, c8->k_scale,
+                                      c8->v_scale, kv_cap, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "block forward: 8-bit cache append");
   }
 
   // a5/a6: attention
   {
     lb::AttnArgs aa{};
-    aa.q = q_buf; aa.k = k_buf; aa.v = v_buf; aa.out = o_buf;
+    aa.q = q_buf; aa.k = c8 ? c8->k8 : k_buf; aa.v = c8 ? c8->v8 : v_buf; aa.out = o_buf;
     aa.positions = has_cache ? positions : nullptr;
     aa.B = B; aa.Tq = T; aa.S = has_cache ? kv_cap : T; aa.nq = nq; aa.nkv = nkv; aa.hd = hd;
     aa.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(hd)));
+    if (c8) {
+      aa.k_scale = c8->k_scale;
+      aa.v_scale = c8->v_scale;
+    }
     e = timed("attention", s, [&](const char** name) {
-      return lb::launch_attention(wdt, aa, attn_ws, p.attn, s, name);
+      return c8 ? lb::launch_attention_fp8kv(aa, attn_ws, p.attn, s, name)
+                : lb::launch_attention(wdt, aa, attn_ws, p.attn, s, name);
     });
-    if (e != hipSuccess) return hip_fail(e, "llama_block_forward: attention");
+    if (e != hipSuccess) return hip_fail(e, "block forward: attention");
   }
 
   // a7: O projection + residual into h
@@ -473,7 +499,7 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
     e = timed("o_resid", s, [&](const char** name) {
       return lb::launch_gemm(wdt, o_buf, M, nq * hd, wo, d, false, ep, gemm_ws, p.gemm, s, name);
     });
-    if (e != hipSuccess) return hip_fail(e, "llama_block_forward: o projection");
+    if (e != hipSuccess) return hip_fail(e, "block forward: o projection");
   }
 
   // a8: FFN pre-norm (f reuses the a buffer)
@@ -481,12 +507,160 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
     *name = "rmsnorm";
     return lb::launch_rmsnorm(h_buf, nullptr, w->ffn_norm, a_buf, nullptr, M, d, feps, wdt, rdt, s);
   });
-  if (e != hipSuccess) return hip_fail(e, "llama_block_forward: ffn norm");
+  if (e != hipSuccess) return hip_fail(e, "block forward: ffn norm");
 
   // a9/a10: SwiGLU FFN + residual into y
   e = run_ffn(a_buf, w->w_gate, w->w_up, w->w_down, h_buf, y, M, d, d_ff, wdt, rdt, mact, gemm_ws, p.gemm, s);
-  if (e != hipSuccess) return hip_fail(e, "llama_block_forward: ffn");
+  if (e != hipSuccess) return hip_fail(e, "block forward: ffn");
   return ok();
+}
+
+}  // namespace
+
+int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
+                        const int32_t* positions, void* k_cache, void* v_cache, int32_t kv_cap,
+                        int32_t batch, int32_t seq_len, int32_t d_model, int32_t n_q_heads,
+                        int32_t n_kv_heads, int32_t head_dim, int32_t d_ff, double rope_theta,
+                        double eps, int wdtype, int rdtype, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  if (!dtype_ok(wdtype) || !dtype_ok(rdtype))
+    return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code (wdtype=%d rdtype=%d)", wdtype, rdtype);
+  int st = check_block_args(x, y, w, positions, batch, seq_len, d_model, n_q_heads, n_kv_heads, head_dim, d_ff,
+                            rope_theta, eps, kv_cap);
+  if (st != LLAMA_OK) return st;
+  const bool has_cache = kv_cap > 0;
+  if (has_cache != (k_cache != nullptr) || has_cache != (v_cache != nullptr))
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "k_cache and v_cache must both be given exactly when kv_cap > 0");
+  if (batch == 0 || seq_len == 0) return ok();
+  for (const void* p : std::initializer_list<const void*>{static_cast<const void*>(k_cache),
+                                                          static_cast<const void*>(v_cache), workspace})
+    if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  return run_block(x, y, w, positions, k_cache, v_cache, kv_cap, batch, seq_len, d_model, n_q_heads, n_kv_heads,
+                   head_dim, d_ff, rope_theta, eps, static_cast<DType>(wdtype), static_cast<DType>(rdtype),
+                   workspace, ws_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// 8-bit KV cache
+// ---------------------------------------------------------------------------
+namespace {
+
+int check_fp8_cache(const void* k8, const void* v8, const float* ks, const float* vs, int32_t kv_cap) {
+  if (kv_cap <= 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "kv_cap must be > 0");
+  if (!k8 || !v8 || !ks || !vs)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "the 8-bit caches and their scales must be non-null");
+  for (const void* p : std::initializer_list<const void*>{k8, v8, static_cast<const void*>(ks),
+                                                          static_cast<const void*>(vs)})
+    if (!aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+int llama_kv_append_fp8(const void* k, const void* v, const int32_t* positions, int32_t batch,
+                        int32_t seq_len, int32_t n_kv_heads, int32_t head_dim, int wdtype, void* k_cache,
+                        void* v_cache, float* k_scale, float* v_scale, int32_t kv_cap, void* stream) {
+  if (!dtype_ok(wdtype)) return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code %d", wdtype);
+  if (batch < 0 || seq_len < 0 || n_kv_heads <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "batch, seq_len must be >= 0 and n_kv_heads > 0");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(LLAMA_ERR_UNSUPPORTED, "the 8-bit cache needs head_dim 64, 128 or 256 (got %d)", head_dim);
+  int st = check_fp8_cache(k_cache, v_cache, k_scale, v_scale, kv_cap);
+  if (st != LLAMA_OK) return st;
+  const int64_t n = static_cast<int64_t>(batch) * seq_len;
+  if (n == 0) return ok();
+  if (!k || !v || !positions) return fail(LLAMA_ERR_INVALID_ARGUMENT, "k, v and positions must be non-null");
+  if (!aligned16(k) || !aligned16(v)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  if (n * n_kv_heads * 2 > 0x7fffffffLL * 4) return fail(LLAMA_ERR_UNSUPPORTED, "too many rows");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("kv_append_fp8", s, [&](const char** name) {
+    *name = "kv_append_fp8";
+    return lb::launch_kv_append_fp8(k, v, positions, n, seq_len, n_kv_heads, head_dim, static_cast<DType>(wdtype),
+                                    k_cache, v_cache, k_scale, v_scale, kv_cap, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_kv_append_fp8");
+  return ok();
+}
+
+size_t llama_gqa_attention_fp8kv_workspace_bytes(int32_t batch, int32_t kv_cap, int32_t n_q_heads,
+                                                 int32_t n_kv_heads, int32_t head_dim) {
+  if (batch <= 0 || kv_cap <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim != 128) return 0;
+  return lb::attention_fp8kv_workspace_bytes(batch, kv_cap, n_q_heads, n_kv_heads);
+}
+
+namespace {
+
+int check_fp8_attention_shape(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
+  int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+  if (st != LLAMA_OK) return st;
+  const int r = n_q_heads / n_kv_heads;
+  if (head_dim != 128 || (r != 1 && r != 2 && r != 4 && r != 8))
+    return fail(LLAMA_ERR_UNSUPPORTED, "the 8-bit cache attention needs head_dim 128 and n_q/n_kv in {1,2,4,8}");
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+int llama_gqa_attention_fp8kv(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                              const float* v_scale, void* out, const int32_t* positions, int32_t batch,
+                              int32_t kv_cap, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (batch < 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "batch must be >= 0");
+  int st = check_fp8_attention_shape(n_q_heads, n_kv_heads, head_dim);
+  if (st != LLAMA_OK) return st;
+  st = check_fp8_cache(k_cache, v_cache, k_scale, v_scale, kv_cap);
+  if (st != LLAMA_OK) return st;
+  if (batch == 0) return ok();
+  if (!q || !out || !positions) return fail(LLAMA_ERR_INVALID_ARGUMENT, "q, out and positions must be non-null");
+  if (out == q) return fail(LLAMA_ERR_INVALID_ARGUMENT, "out must not alias q");
+  for (const void* p : std::initializer_list<const void*>{q, static_cast<const void*>(out), workspace})
+    if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  const size_t need = llama_gqa_attention_fp8kv_workspace_bytes(batch, kv_cap, n_q_heads, n_kv_heads, head_dim);
+  if (ws_bytes < need || !workspace)
+    return fail(LLAMA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  lb::AttnArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.out = out; a.positions = positions;
+  a.B = batch; a.Tq = 1; a.S = kv_cap; a.nq = n_q_heads; a.nkv = n_kv_heads; a.hd = head_dim;
+  a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(head_dim)));
+  a.k_scale = k_scale; a.v_scale = v_scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("attention", s, [&](const char** name) {
+    return lb::launch_attention_fp8kv(a, workspace, ws_bytes, s, name);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_gqa_attention_fp8kv");
+  return ok();
+}
+
+size_t llama_block_forward_fp8kv_workspace_bytes(int32_t batch, int32_t d_model, int32_t n_q_heads,
+                                                 int32_t n_kv_heads, int32_t head_dim, int32_t d_ff,
+                                                 int32_t kv_cap, int rdtype) {
+  if (batch <= 0 || d_model <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || d_ff <= 0 ||
+      kv_cap <= 0 || !dtype_ok(rdtype))
+    return 0;
+  return block_plan(batch, 1, d_model, n_q_heads, n_kv_heads, head_dim, d_ff, kv_cap, DType::BF16,
+                    static_cast<DType>(rdtype), true)
+      .total;
+}
+
+int llama_block_forward_fp8kv(const void* x, void* y, const llama_block_weights* w, const int32_t* positions,
+                              void* k_cache, void* v_cache, float* k_scale, float* v_scale, int32_t kv_cap,
+                              int32_t batch, int32_t d_model, int32_t n_q_heads, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t d_ff, double rope_theta, double eps, int rdtype,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(rdtype)) return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code (rdtype=%d)", rdtype);
+  int st = check_block_args(x, y, w, positions, batch, 1, d_model, n_q_heads, n_kv_heads, head_dim, d_ff,
+                            rope_theta, eps, kv_cap);
+  if (st != LLAMA_OK) return st;
+  st = check_fp8_attention_shape(n_q_heads, n_kv_heads, head_dim);
+  if (st != LLAMA_OK) return st;
+  st = check_fp8_cache(k_cache, v_cache, k_scale, v_scale, kv_cap);
+  if (st != LLAMA_OK) return st;
+  if (batch == 0) return ok();
+  if (workspace && !aligned16(workspace)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  const Fp8Cache c8{k_cache, v_cache, k_scale, v_scale};
+  return run_block(x, y, w, positions, nullptr, nullptr, kv_cap, batch, 1, d_model, n_q_heads, n_kv_heads,
+                   head_dim, d_ff, rope_theta, eps, DType::BF16, static_cast<DType>(rdtype), workspace, ws_bytes,
+                   static_cast<hipStream_t>(stream), &c8);
 }
 
 // ---------------------------------------------------------------------------

@@ -573,10 +573,21 @@ __device__ __forceinline__ float rows_max(float x) {
 
 // K/V registers of one 32-slot step: K as two 16-slot MFMA A blocks x 4
 // head-dim steps, V as 8 slots per lane group (16 lanes per 256-byte row).
-struct DecRegs {
+// With the 8-bit cache (KV8) a lane holds 32 E4M3 codes of each K row block
+// (the four head-dim steps), 8 codes of each V row and the fp32 row scales of
+// the eight slots whose scores it computes.
+template <bool KV8>
+struct DecRegsT {
   u32x4 k[2][4];
   u32x4 v[8];
 };
+template <>
+struct DecRegsT<true> {
+  u32x4 k[2][2];
+  u32x2 v[8];
+  float sc;  // lane l < 32: k scale of slot js + l; l >= 32: v scale of slot js + l - 32
+};
+using DecRegs = DecRegsT<false>;
 
 __device__ __forceinline__ void dec_load(DecRegs& r, const bf16_t* kbase, const bf16_t* vbase,
                                          int64_t kvrow, int js, int jend, int col, int grp) {
@@ -591,6 +602,76 @@ __device__ __forceinline__ void dec_load(DecRegs& r, const bf16_t* kbase, const 
     const int j = min(js + grp + 4 * i, jend);
     r.v[i] = *reinterpret_cast<const u32x4*>(vbase + j * kvrow + col * 8);
   }
+}
+
+// 8-bit cache rows: codes [n_kv][S][128] per sequence (the slots of one KV
+// head are contiguous 128-byte rows), scales [n_kv][S].  Lane (col, grp) loads the 32
+// codes grp*32 .. grp*32+31 of K row js + blk*16 + col (head-dim steps s use
+// codes s*8 .. s*8+7 of them, so the Q fragments take the same permutation of
+// the head dimension) and the 8 codes col*8 .. col*8+7 of V row js + grp + 4i.
+// The rows of one (sequence, KV head) are read through buffer resources that
+// end after its last visible slot: rows past the end read as zero (their
+// scores are masked), so no clamping runs per load.  The range check covers
+// the per-lane offset only (not the scalar one), so each load's offset is
+// the lane's fixed row offset plus the step's js * row stride.
+struct Dec8Src {
+  __amdgpu_buffer_rsrc_t k, v;
+  uint32_t row;      // bytes between slots (128)
+  uint32_t koff[2];  // lane offsets of the two 16-slot K blocks
+  uint32_t voff[8];  // lane offsets of the eight V rows
+  const float* ksb;
+  const float* vsb;
+
+  __device__ __forceinline__ void init(const uint8_t* k8, const uint8_t* v8, const float* ks, const float* vs,
+                                       int vis, int col, int grp) {
+    row = 128u;
+    const uint32_t bytes = vis >= 0 ? static_cast<uint32_t>(vis) * row + 128u : 0u;
+    k = make_rsrc(k8, bytes);
+    v = make_rsrc(v8, bytes);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) koff[blk] = static_cast<uint32_t>(blk * 16 + col) * row + grp * 32;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) voff[i] = static_cast<uint32_t>(grp + 4 * i) * row + col * 8;
+    ksb = ks;
+    vsb = vs;
+  }
+};
+
+__device__ __forceinline__ void dec_load8(DecRegsT<true>& r, const Dec8Src& src, int js, int jend, int col,
+                                          int grp) {
+  const uint32_t so = static_cast<uint32_t>(js) * src.row;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    r.k[blk][0] = buffer_load16(src.k, src.koff[blk] + so, 0);
+    r.k[blk][1] = buffer_load16(src.k, src.koff[blk] + so + 16u, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    r.v[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(src.v, src.voff[i] + so, 0, 0));
+  // the step's 32 k scales and 32 v scales, one per lane (masked slots read a
+  // visible one); step() hands them to the score lanes through LDS
+  const int l = col + 16 * grp;
+  r.sc = (l < 32 ? src.ksb : src.vsb)[min(js + (l & 31), jend)];
+}
+
+// Eight E4M3 codes (the lowest byte first) -> eight bf16 / fp32 values.  The
+// conversion is exact: every E4M3 value is a bf16 value, so the upper halves
+// of the fp32 results are the bf16 encodings.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t d0, uint32_t d1) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(d0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(d0, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(d1, false), e = __builtin_amdgcn_cvt_pk_f32_fp8(d1, true);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  r[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+  r[3] = __builtin_amdgcn_perm(__float_as_uint(e[1]), __float_as_uint(e[0]), 0x07060302u);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+__device__ __forceinline__ void fp8x8_to_f32(uint32_t d0, uint32_t d1, float v[8]) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(d0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(d0, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(d1, false), e = __builtin_amdgcn_cvt_pk_f32_fp8(d1, true);
+  v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
+  v[4] = c[0]; v[5] = c[1]; v[6] = e[0]; v[7] = e[1];
 }
 
 template <int R>
@@ -608,17 +689,44 @@ struct DecState {
       for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
   }
 
-  // one 32-slot step: scores on the matrix cores, online softmax, PV on the VALU
-  __device__ __forceinline__ void step(const DecRegs& kv, const bf16x8_t (&qf)[4], float c, int js, int jend,
+  // one 32-slot step: scores on the matrix cores, online softmax, PV on the VALU.
+  // With the 8-bit cache a score is k_scale * (q . codes) and a weight enters
+  // PV as p * v_scale (the softmax sum uses p itself).
+  template <bool KV8>
+  __device__ __forceinline__ void step(const DecRegsT<KV8>& kv, const bf16x8_t (&qf)[4], float c, int js, int jend,
                                        int col, int grp, float (*s_p)[RP], float* s_alpha) {
+    f32x4 ks[2], vs[2];
+    if constexpr (KV8) {
+      // the weight buffer (>= 64 floats) first passes the scales: score lane
+      // (col, grp) needs those of slots blk*16 + grp*4 .. +3.  LDS accesses of
+      // a wavefront run in order, so the previous step's weight reads are done
+      // and this step's weight writes come after these reads.
+      float* sbuf = &s_p[0][0];
+      sbuf[col + 16 * grp] = kv.sc;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        ks[blk] = *reinterpret_cast<const f32x4*>(sbuf + blk * 16 + grp * 4);
+        vs[blk] = *reinterpret_cast<const f32x4*>(sbuf + 32 + blk * 16 + grp * 4);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
     f32x4 sc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv.k[blk][s]), qf[s], sc[blk],
-                                                          0, 0, 0);
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t kf;
+        if constexpr (KV8) {
+          const u32x4 src = kv.k[blk][s >> 1];
+          kf = fp8x8_to_bf16(src[(s & 1) * 2], src[(s & 1) * 2 + 1]);
+        } else {
+          kf = __builtin_bit_cast(bf16x8_t, kv.k[blk][s]);
+        }
+        sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc[blk], 0, 0, 0);
+      }
+      if constexpr (KV8) sc[blk] *= ks[blk];
     }
     float tmax = -INFINITY;
 #pragma unroll
@@ -640,7 +748,9 @@ struct DecState {
       for (int i = 0; i < 4; ++i) {
         const float p = fast_exp2(__builtin_fmaf(sc[blk][i], c, -m_new));
         psum += p;
-        if (col < R) s_p[blk * 16 + grp * 4 + i][col] = p;
+        float pv = p;
+        if constexpr (KV8) pv *= vs[blk][i];
+        if (col < R) s_p[blk * 16 + grp * 4 + i][col] = pv;
       }
     l_run = l_run * alpha + rows_sum(psum);
     if (grp == 0 && col < R) s_alpha[col] = alpha;
@@ -655,10 +765,14 @@ struct DecState {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float v[8];
+      if constexpr (KV8) {
+        fp8x8_to_f32(kv.v[i][0], kv.v[i][1], v);
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] = __uint_as_float(kv.v[i][q] << 16);
-        v[2 * q + 1] = __uint_as_float(kv.v[i][q] & 0xffff0000u);
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] = __uint_as_float(kv.v[i][q] << 16);
+          v[2 * q + 1] = __uint_as_float(kv.v[i][q] & 0xffff0000u);
+        }
       }
       const int sl = grp + 4 * i;
 #pragma unroll
@@ -672,7 +786,7 @@ struct DecState {
   }
 };
 
-template <int R>
+template <int R, bool KV8>
 __global__ void __launch_bounds__(256)
 attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__ part_o,
                     float* __restrict__ part_ml) {
@@ -692,10 +806,19 @@ attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__
   if (j0 > vis) return;  // nothing visible (the combine skips this chunk)
   const int jend = min(vis, j0 + CHUNK - 1);
 
+  // K/V rows of (b, g): bf16 elements, or E4M3 codes (one byte each) plus
+  // the fp32 row scales [n_kv][S] of the sequence
   const int64_t kvrow = static_cast<int64_t>(a.nkv) * HD;
-  const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
-  const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
+  const int64_t kvoff = (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
+  const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + kvoff;
+  const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + kvoff;
   const int col = lane & 15, grp = lane >> 4;
+  Dec8Src src8;
+  if constexpr (KV8) {
+    const int64_t hs = (static_cast<int64_t>(b) * a.nkv + g) * a.S;  // (sequence, KV head) slot base
+    src8.init(static_cast<const uint8_t*>(a.k) + hs * HD, static_cast<const uint8_t*>(a.v) + hs * HD,
+              a.k_scale + hs, a.v_scale + hs, vis, col, grp);
+  }
 
   // Q^T fragments (B operand): column = query head col (< R), k = head dim
   bf16x8_t qf[4];
@@ -703,7 +826,9 @@ attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__
     const bf16_t* qp = static_cast<const bf16_t*>(a.q) + (static_cast<int64_t>(b) * a.nq + g * R + (col < R ? col : 0)) * HD;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 t = *reinterpret_cast<const u32x4*>(qp + s * 32 + grp * 8);
+      // head-dim step s, lane group grp: elements s*32 + grp*8 .. +7, or with
+      // the 8-bit cache grp*32 + s*8 .. +7 (the permutation of its K codes)
+      u32x4 t = *reinterpret_cast<const u32x4*>(qp + (KV8 ? grp * 32 + s * 8 : s * 32 + grp * 8));
       if (col >= R) t = u32x4{0, 0, 0, 0};
       qf[s] = __builtin_bit_cast(bf16x8_t, t);
     }
@@ -711,10 +836,25 @@ attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__
   const float c = a.scale * kLog2e;
   St st;
   st.init();
-  for (int js = j0; js <= jend; js += SUB) {
-    DecRegs rr;
-    dec_load(rr, kbase, vbase, kvrow, js, jend, col, grp);
-    st.step(rr, qf, c, js, jend, col, grp, s_p[w], s_alpha[w]);
+  if constexpr (KV8) {
+    // half the bytes per slot: the next step's loads are issued before this
+    // step's arithmetic so that each wavefront keeps two steps in flight
+    // (loads past the end re-read the last visible slot)
+    DecRegsT<true> ra, rb;
+    if (j0 <= jend) dec_load8(ra, src8, j0, jend, col, grp);
+    for (int js = j0; js <= jend; js += 2 * SUB) {
+      dec_load8(rb, src8, js + SUB, jend, col, grp);
+      st.step(ra, qf, c, js, jend, col, grp, s_p[w], s_alpha[w]);
+      if (js + SUB > jend) break;
+      dec_load8(ra, src8, js + 2 * SUB, jend, col, grp);
+      st.step(rb, qf, c, js + SUB, jend, col, grp, s_p[w], s_alpha[w]);
+    }
+  } else {
+    for (int js = j0; js <= jend; js += SUB) {
+      DecRegs rr;
+      dec_load(rr, kbase, vbase, kvrow, js, jend, col, grp);
+      st.step(rr, qf, c, js, jend, col, grp, s_p[w], s_alpha[w]);
+    }
   }
 
   // reduce o over the 4 lane groups, then lanes 0..15 write the partial
@@ -749,9 +889,10 @@ attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__
 // are resident at once; nothing goes through HBM but K, V, q and the output.
 // ===========================================================================
 // At most 16 wavefronts per workgroup (8 for R = 8, whose accumulators need
-// more than the 128 registers a 16-wavefront workgroup leaves per lane).
-template <int R>
-__global__ void __launch_bounds__(R >= 8 ? 512 : 1024)
+// more than the 128 registers a 16-wavefront workgroup leaves per lane, and
+// for the 8-bit cache, whose two steps of registers in flight need more too).
+template <int R, bool KV8>
+__global__ void __launch_bounds__(R >= 8 || KV8 ? 512 : 1024)
 attn_decode3_kernel(AttnArgs a) {
   constexpr int HD = 128, SUB = kDSub;
   using St = DecState<R>;
@@ -768,16 +909,27 @@ attn_decode3_kernel(AttnArgs a) {
   const int j0 = w * per;
   const int jend = min(vis, j0 + per - 1);
 
+  // K/V rows of (b, g): bf16 elements, or E4M3 codes (one byte each) plus
+  // the fp32 row scales [n_kv][S] of the sequence
   const int64_t kvrow = static_cast<int64_t>(a.nkv) * HD;
-  const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
-  const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
+  const int64_t kvoff = (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
+  const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + kvoff;
+  const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + kvoff;
   const int col = lane & 15, grp = lane >> 4;
+  Dec8Src src8;
+  if constexpr (KV8) {
+    const int64_t hs = (static_cast<int64_t>(b) * a.nkv + g) * a.S;  // (sequence, KV head) slot base
+    src8.init(static_cast<const uint8_t*>(a.k) + hs * HD, static_cast<const uint8_t*>(a.v) + hs * HD,
+              a.k_scale + hs, a.v_scale + hs, vis, col, grp);
+  }
   bf16x8_t qf[4];
   {
     const bf16_t* qp = static_cast<const bf16_t*>(a.q) + (static_cast<int64_t>(b) * a.nq + g * R + (col < R ? col : 0)) * HD;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 t = *reinterpret_cast<const u32x4*>(qp + s * 32 + grp * 8);
+      // head-dim step s, lane group grp: elements s*32 + grp*8 .. +7, or with
+      // the 8-bit cache grp*32 + s*8 .. +7 (the permutation of its K codes)
+      u32x4 t = *reinterpret_cast<const u32x4*>(qp + (KV8 ? grp * 32 + s * 8 : s * 32 + grp * 8));
       if (col >= R) t = u32x4{0, 0, 0, 0};
       qf[s] = __builtin_bit_cast(bf16x8_t, t);
     }
@@ -786,10 +938,25 @@ attn_decode3_kernel(AttnArgs a) {
   St st;
   st.init();
   float* my_alpha = s_ml + w * R * 2;  // scratch for the step's rescale factors (before the final write)
-  for (int js = j0; js <= jend; js += SUB) {
-    DecRegs rr;
-    dec_load(rr, kbase, vbase, kvrow, js, jend, col, grp);
-    st.step(rr, qf, c, js, jend, col, grp, s_p[w], my_alpha);
+  if constexpr (KV8) {
+    // half the bytes per slot: the next step's loads are issued before this
+    // step's arithmetic so that each wavefront keeps two steps in flight
+    // (loads past the end re-read the last visible slot)
+    DecRegsT<true> ra, rb;
+    if (j0 <= jend) dec_load8(ra, src8, j0, jend, col, grp);
+    for (int js = j0; js <= jend; js += 2 * SUB) {
+      dec_load8(rb, src8, js + SUB, jend, col, grp);
+      st.step(ra, qf, c, js, jend, col, grp, s_p[w], my_alpha);
+      if (js + SUB > jend) break;
+      dec_load8(ra, src8, js + 2 * SUB, jend, col, grp);
+      st.step(rb, qf, c, js + SUB, jend, col, grp, s_p[w], my_alpha);
+    }
+  } else {
+    for (int js = j0; js <= jend; js += SUB) {
+      DecRegs rr;
+      dec_load(rr, kbase, vbase, kvrow, js, jend, col, grp);
+      st.step(rr, qf, c, js, jend, col, grp, s_p[w], my_alpha);
+    }
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -883,12 +1050,12 @@ int device_cus() {
 
 constexpr size_t kD3MaxLds = 64 * 1024;
 
-template <int R>
-constexpr int d3_max_waves() { return R >= 8 ? 8 : 16; }
+template <int R, bool KV8>
+constexpr int d3_max_waves() { return R >= 8 || KV8 ? 8 : 16; }
 
 // Workgroups of attn_decode3_kernel<R> with nw wavefronts that one CU holds
 // at once (register, LDS and wave-slot limits), cached per device.
-template <int R>
+template <int R, bool KV8>
 int d3_blocks_per_cu(int nw) {
   static thread_local int cached_dev = -1;
   static thread_local int cache[17];
@@ -900,7 +1067,7 @@ int d3_blocks_per_cu(int nw) {
   }
   if (cache[nw] < 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_decode3_kernel<R>, 64 * nw,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_decode3_kernel<R, KV8>, 64 * nw,
                                                      decode3_lds_bytes(R, nw)) != hipSuccess)
       n = 0;
     cache[nw] = n;
@@ -917,39 +1084,39 @@ constexpr int kDecWavesPerCu = 6;
 
 // Wavefronts per (sequence, KV head) workgroup of attn_decode3_kernel: close
 // to the target count, all workgroups resident in one round, within LDS.
-template <int R>
+template <int R, bool KV8>
 int d3_pick_waves(int64_t pairs, int64_t target) {
   const int cus = device_cus();
-  int nw = static_cast<int>(std::min<int64_t>(d3_max_waves<R>(), std::max<int64_t>(1, (target + pairs / 2) / pairs)));
+  int nw = static_cast<int>(std::min<int64_t>(d3_max_waves<R, KV8>(), std::max<int64_t>(1, (target + pairs / 2) / pairs)));
   while (nw > 1 && (decode3_lds_bytes(R, nw) > kD3MaxLds ||
-                    pairs > static_cast<int64_t>(d3_blocks_per_cu<R>(nw)) * cus))
+                    pairs > static_cast<int64_t>(d3_blocks_per_cu<R, KV8>(nw)) * cus))
     --nw;
   return nw;
 }
 
-template <int R>
+template <int R, bool KV8>
 hipError_t launch_decode_bf16(const AttnArgs& a, void* ws, hipStream_t s, const char** kernel_name) {
   constexpr int HD = 128;
   const int64_t pairs = static_cast<int64_t>(a.B) * a.nkv;
   const int64_t target = static_cast<int64_t>(device_cus()) * kDecWavesPerCu;
-  const int nw = d3_pick_waves<R>(pairs, target);
+  const int nw = d3_pick_waves<R, KV8>(pairs, target);
   if (pairs * nw * 2 >= target) {
     // one workgroup per (sequence, KV head) reaches at least half the target
-    if (kernel_name) *kernel_name = "attn_decode_wg";
-    hipLaunchKernelGGL((attn_decode3_kernel<R>), dim3(static_cast<unsigned>(pairs)), dim3(64 * nw),
+    if (kernel_name) *kernel_name = KV8 ? "attn_decode_wg_fp8kv" : "attn_decode_wg";
+    hipLaunchKernelGGL((attn_decode3_kernel<R, KV8>), dim3(static_cast<unsigned>(pairs)), dim3(64 * nw),
                        decode3_lds_bytes(R, nw), s, a);
     return hipGetLastError();
   }
   // few pairs (long contexts, small batches): split the slots of each pair
   // into chunks across wavefronts of their own, then merge the partials
-  if (kernel_name) *kernel_name = "attn_decode_splitk";
+  if (kernel_name) *kernel_name = KV8 ? "attn_decode_splitk_fp8kv" : "attn_decode_splitk";
   const int64_t want = std::max<int64_t>(1, target / pairs);
   int chunk = static_cast<int>(((a.S + want - 1) / want + kDSub - 1) / kDSub * kDSub);
   chunk = std::max(chunk, kDChunk);  // never more chunks than the workspace holds
   const int nch = (a.S + chunk - 1) / chunk;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + static_cast<int64_t>(a.B) * a.nq * nch * HD;
-  hipLaunchKernelGGL((attn_decode2_kernel<R>), dim3(static_cast<unsigned>((pairs * nch + 3) / 4)), dim3(256), 0, s,
+  hipLaunchKernelGGL((attn_decode2_kernel<R, KV8>), dim3(static_cast<unsigned>((pairs * nch + 3) / 4)), dim3(256), 0, s,
                      a, nch, chunk, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -966,10 +1133,10 @@ hipError_t launch_decode_t(const AttnArgs& a, void* ws, hipStream_t s, const cha
   const int R = a.nq / a.nkv;
   if (sizeof(T) == 2 && HD == 128) {
     switch (R) {
-      case 1: return launch_decode_bf16<1>(a, ws, s, kernel_name);
-      case 2: return launch_decode_bf16<2>(a, ws, s, kernel_name);
-      case 4: return launch_decode_bf16<4>(a, ws, s, kernel_name);
-      case 8: return launch_decode_bf16<8>(a, ws, s, kernel_name);
+      case 1: return launch_decode_bf16<1, false>(a, ws, s, kernel_name);
+      case 2: return launch_decode_bf16<2, false>(a, ws, s, kernel_name);
+      case 4: return launch_decode_bf16<4, false>(a, ws, s, kernel_name);
+      case 8: return launch_decode_bf16<8, false>(a, ws, s, kernel_name);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1016,6 +1183,26 @@ size_t attention_workspace_bytes(DType dt, int B, int Tq, int S, int nq, int nkv
   if (!decode_supported(dt, a)) return 0;
   const int nch = decode_chunks(S);
   return static_cast<size_t>(B) * nq * nch * (hd + 2) * sizeof(float);
+}
+
+size_t attention_fp8kv_workspace_bytes(int B, int S, int nq, int nkv) {
+  return static_cast<size_t>(B) * nq * decode_chunks(S) * (128 + 2) * sizeof(float);
+}
+
+hipError_t launch_attention_fp8kv(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
+                                  const char** kernel_name) {
+  if (a.B == 0) return hipSuccess;
+  if (a.Tq != 1 || a.hd != 128 || !a.k_scale || !a.v_scale) return hipErrorInvalidValue;
+  if (ws_bytes < attention_fp8kv_workspace_bytes(a.B, a.S, a.nq, a.nkv)) return hipErrorInvalidValue;
+  // (the buffer resources address one KV head's rows with 32-bit offsets)
+  if (static_cast<int64_t>(a.S) * 128 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  switch (a.nq / a.nkv) {
+    case 1: return launch_decode_bf16<1, true>(a, ws, s, kernel_name);
+    case 2: return launch_decode_bf16<2, true>(a, ws, s, kernel_name);
+    case 4: return launch_decode_bf16<4, true>(a, ws, s, kernel_name);
+    case 8: return launch_decode_bf16<8, true>(a, ws, s, kernel_name);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attention(DType dt, const AttnArgs& a, void* ws, size_t ws_bytes,

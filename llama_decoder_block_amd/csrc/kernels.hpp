@@ -298,11 +298,31 @@ struct AttnArgs {
   const int32_t* positions;  // [B, Tq] or null (query t sees 0..t)
   int B, Tq, S, nq, nkv, hd;
   float scale;         // 1/sqrt(hd)
+  const float* k_scale;  // 8-bit cache only: fp32 row scales [B, nkv, S] of k and v
+  const float* v_scale;
 };
 
 size_t attention_workspace_bytes(DType dt, int B, int Tq, int S, int nq, int nkv, int hd);
 
 hipError_t launch_attention(DType dt, const AttnArgs& a, void* ws, size_t ws_bytes,
                             hipStream_t s, const char** kernel_name);
+
+// ---------------------------------------------------------------------------
+// 8-bit KV cache: E4M3 codes [B, nkv, S, hd] (one byte per element; the slots
+// of one KV head are contiguous) with one fp32 scale per (sequence, KV head,
+// slot) in [B, nkv, S].
+// ---------------------------------------------------------------------------
+// Decode attention (Tq == 1, hd == 128, bf16 q and out) over the 8-bit cache
+// a.k / a.v with scales a.k_scale / a.v_scale.
+size_t attention_fp8kv_workspace_bytes(int B, int S, int nq, int nkv);
+hipError_t launch_attention_fp8kv(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
+                                  const char** kernel_name);
+
+// Quantizes rows k, v [n_tokens, nkv, hd] (dtype dt) and stores them at slot
+// positions[n] of sequence n / seq_len (tokens whose slot is outside
+// [0, kv_cap) are skipped).  hd must be a multiple of 64, at most 256.
+hipError_t launch_kv_append_fp8(const void* k, const void* v, const int32_t* positions, int64_t n_tokens,
+                                int seq_len, int nkv, int hd, DType dt, void* k8, void* v8, float* k_scale,
+                                float* v_scale, int kv_cap, hipStream_t s);
 
 }  // namespace lb

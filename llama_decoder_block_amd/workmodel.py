@@ -81,6 +81,16 @@ def decode_attention_bytes(s, batch, attend_len, elem_bytes=2):
     return batch * attend_len * kv_bytes_per_token(s, elem_bytes)
 
 
+# 8-bit KV cache: one byte per element plus one fp32 scale per row of head_dim
+# elements (per slot, KV head and K or V)
+FP8KV_BYTES_PER_ELEM = "fp8"
+
+
+def decode_attention_bytes_fp8kv(s, batch, attend_len):
+    """Codes of every visible K/V slot plus their row scales, read once."""
+    return batch * attend_len * 2 * s.n_kv * (s.head_dim + 4)
+
+
 def decode_weight_bytes(s, elem_bytes=2):
     return block_params(s) * elem_bytes
 
@@ -89,7 +99,7 @@ def gemm_flops(m, n, k):
     return 2 * m * n * k
 
 
-def step_work(s, batch, seq, attend_len=None, wbytes=2, rbytes=4):
+def step_work(s, batch, seq, attend_len=None, wbytes=2, rbytes=4, kv_bytes=None):
     """Algorithmic FLOPs and HBM bytes of each step of one block forward.
 
     Returns {step: (flops, bytes)} keyed like the library's timing records
@@ -99,7 +109,8 @@ def step_work(s, batch, seq, attend_len=None, wbytes=2, rbytes=4):
     one-token decode.  Bytes: every weight, input and output read or written
     once; for decode attention only the K/V slots are counted (the query and
     output are 1/4000 of it).  `wbytes` / `rbytes` are the element sizes of
-    the GEMM operands and of the residual stream.
+    the GEMM operands and of the residual stream; kv_bytes=FP8KV_BYTES_PER_ELEM
+    counts the decode cache as 8-bit codes plus row scales.
     """
     m = batch * seq
     d, hd = s.d_model, s.head_dim
@@ -112,8 +123,9 @@ def step_work(s, batch, seq, attend_len=None, wbytes=2, rbytes=4):
     if attend_len is None:
         out["attention"] = (prefill_attention_flops(s, batch, seq), m * (nqkv + nqo) * wbytes)
     else:
-        out["attention"] = (decode_attention_flops(s, batch, attend_len),
-                            decode_attention_bytes(s, batch, attend_len, wbytes))
+        kvb = (decode_attention_bytes_fp8kv(s, batch, attend_len) if kv_bytes == FP8KV_BYTES_PER_ELEM
+               else decode_attention_bytes(s, batch, attend_len, wbytes))
+        out["attention"] = (decode_attention_flops(s, batch, attend_len), kvb)
     out["o_resid"] = (gemm_flops(m, d, nqo), (d * nqo + m * nqo) * wbytes + 2 * m * d * rbytes)
     out["ffn_norm"] = (0, norm_bytes)
     out["gate_up_silu"] = (gemm_flops(m, 2 * s.d_ff, d), (2 * s.d_ff * d + m * d + m * s.d_ff) * wbytes)

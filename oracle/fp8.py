@@ -102,14 +102,44 @@ def dequantize_rows(codes, scales):
 
 
 def kv_cache_from_rows(k_rows, v_rows):
-    """Quantize bf16-valued K / V caches [B, S, n_kv, hd]; returns
-    (k_codes, v_codes [B, S, n_kv, hd] uint8, k_scales, v_scales [B, n_kv, S]
-    float32) in the layouts of the 8-bit cache."""
-    kc, ks = quantize_rows(k_rows)
-    vc, vs = quantize_rows(v_rows)
-    return kc, vc, np.ascontiguousarray(ks.transpose(0, 2, 1)), np.ascontiguousarray(vs.transpose(0, 2, 1))
+    """Quantize bf16-valued K / V caches [B, S, n_kv, hd] (the token-major
+    layout of the bf16 caches); returns (k_codes, v_codes [B, n_kv, S, hd]
+    uint8, k_scales, v_scales [B, n_kv, S] float32), the head-major layout of
+    the 8-bit cache."""
+    kh = np.asarray(k_rows, dtype=np.float64).transpose(0, 2, 1, 3)
+    vh = np.asarray(v_rows, dtype=np.float64).transpose(0, 2, 1, 3)
+    kc, ks = quantize_rows(kh)
+    vc, vs = quantize_rows(vh)
+    return tuple(np.ascontiguousarray(a) for a in (kc, vc, ks, vs))
 
 
 def kv_cache_values(codes, scales):
-    """codes [B, S, n_kv, hd] with scales [B, n_kv, S] -> float64 [B, S, n_kv, hd]."""
-    return dequantize_rows(codes, np.asarray(scales).transpose(0, 2, 1))
+    """codes [B, n_kv, S, hd] with scales [B, n_kv, S] -> float64 values in
+    the token-major layout [B, S, n_kv, hd] that attention reads."""
+    return dequantize_rows(codes, scales).transpose(0, 2, 1, 3)
+
+
+def decode_step_fp8kv(x, w, position, k_codes, v_codes, k_scales, v_scales, theta, eps, n_q, n_kv):
+    """One decode step of the block against an 8-bit cache, with the bf16
+    path's storage points: the new token's rotated k and its v (rounded to
+    bf16) are quantized into slot ``position[b]`` of sequence b, then query b
+    attends the dequantized slots 0..position[b]; everything else is the
+    plain block ([LA] "Step 2"; [L3] §七, §九).
+    x [B, 1, d]; caches as in :func:`kv_cache_from_rows`.  Returns
+    (y, k_codes, v_codes, k_scales, v_scales) with the updated cache copies."""
+    from . import reference as ref
+    x = np.asarray(x, dtype=np.float64)
+    B = x.shape[0]
+    pos = np.asarray(position, dtype=np.int64).reshape(B, 1)
+    q, k, v = ref._attention_inputs(x, w, pos, theta, eps, n_q, n_kv, True)
+    kc, vc = np.array(k_codes, copy=True), np.array(v_codes, copy=True)
+    ks, vs = np.array(k_scales, copy=True), np.array(v_scales, copy=True)
+    nk, sk = quantize_rows(k[:, 0])      # [B, n_kv, hd], [B, n_kv]
+    nv, sv = quantize_rows(v[:, 0])
+    for b in range(B):
+        p = pos[b, 0]
+        kc[b, :, p], vc[b, :, p] = nk[b], nv[b]
+        ks[b, :, p], vs[b, :, p] = sk[b], sv[b]
+    o = ref.gqa_attention(q, kv_cache_values(kc, ks), kv_cache_values(vc, vs), pos).reshape(B, 1, -1)
+    _, y = ref._block_tail(x, o, w, eps, True)
+    return y, kc, vc, ks, vs

@@ -23,7 +23,7 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced (validation fails first)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(llama_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(llama_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_five_entry_points():
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = binding.lib()
-    assert L.llama_version() == 10000
+    assert L.llama_version() == 10100
     assert L.llama_status_string(0) == b"ok"
     assert L.llama_status_string(-3) == b"workspace too small"
     assert L.llama_status_string(7) == b"unknown status"
@@ -164,3 +164,43 @@ def test_profile_query_unknown():
     n = ctypes.c_int64()
     ms = ctypes.c_double()
     assert L.llama_profile_query(b"no_such_kernel", ctypes.byref(n), ctypes.byref(ms)) == -1
+
+
+def test_fp8kv_validation():
+    L = binding.lib()
+    # append: head_dim must be 64/128/256; caches and capacity required
+    assert L.llama_kv_append_fp8(FAKE, FAKE, FAKE, 2, 1, 8, 96, 1, FAKE, FAKE, FAKE, FAKE, 16, None) == -2
+    assert L.llama_kv_append_fp8(FAKE, FAKE, FAKE, 2, 1, 8, 128, 1, None, FAKE, FAKE, FAKE, 16, None) == -1
+    assert L.llama_kv_append_fp8(FAKE, FAKE, FAKE, 2, 1, 8, 128, 1, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+    assert L.llama_kv_append_fp8(FAKE, FAKE, None, 2, 1, 8, 128, 1, FAKE, FAKE, FAKE, FAKE, 16, None) == -1
+    assert L.llama_kv_append_fp8(FAKE, FAKE, FAKE, 2, 1, 8, 128, 9, FAKE, FAKE, FAKE, FAKE, 16, None) == -2
+
+    def att(**kw):
+        a = dict(q=FAKE, k=FAKE + 0x100, v=FAKE + 0x200, ks=FAKE + 0x300, vs=FAKE + 0x400, out=FAKE + 0x500,
+                 pos=FAKE + 0x600, B=2, cap=100, nq=8, nkv=2, hd=128, ws=FAKE + 0x700, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.llama_gqa_attention_fp8kv(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["out"], a["pos"], a["B"],
+                                           a["cap"], a["nq"], a["nkv"], a["hd"], a["ws"], a["ws_bytes"], None)
+    assert att(hd=64) == -2                 # only head_dim 128
+    assert att(nq=24, nkv=2) == -2          # n_q / n_kv = 12
+    assert att(nkv=3) == -1
+    assert att(ks=None) == -1
+    assert att(cap=0) == -1
+    assert att(pos=None) == -1
+    assert att(out=FAKE) == -1              # out aliases q
+    assert att(k=FAKE + 0x104) == -2        # misaligned
+    need = L.llama_gqa_attention_fp8kv_workspace_bytes(2, 100, 8, 2, 128)
+    assert need > 0 and L.llama_gqa_attention_fp8kv_workspace_bytes(2, 100, 8, 2, 64) == 0
+    assert att(ws_bytes=need - 1) == -3
+    # block: the same shape limits; workspace reported for the decode step
+    w = binding.BlockWeights(*([FAKE + 0x1000 * i for i in range(1, 10)]))
+    need_b = L.llama_block_forward_fp8kv_workspace_bytes(4, 256, 4, 2, 128, 512, 64, 0)
+    assert need_b > 0
+    rc = L.llama_block_forward_fp8kv(FAKE, FAKE + 0x100, ctypes.byref(w), FAKE + 0x200, FAKE + 0x300, FAKE + 0x400,
+                                     FAKE + 0x500, FAKE + 0x600, 64, 4, 256, 4, 2, 64, 512, 1e4, 1e-5, 0,
+                                     FAKE + 0x700, need_b, None)
+    assert rc == -2                         # head_dim 64
+    rc = L.llama_block_forward_fp8kv(FAKE, FAKE + 0x100, ctypes.byref(w), FAKE + 0x200, FAKE + 0x300, FAKE + 0x400,
+                                     FAKE + 0x500, FAKE + 0x600, 64, 4, 256, 4, 2, 128, 512, 1e4, 1e-5, 0,
+                                     FAKE + 0x700, need_b - 1, None)
+    assert rc == -3

@@ -1,0 +1,212 @@
+"""8-bit KV cache on the GPU against the oracle (oracle/fp8.py; the format
+and scale convention are stated in include/llama_block.h).  Needs a GPU.
+
+* the cache writer is bit-exact: codes and scales equal the oracle's for the
+  same bf16 / fp32 rows;
+* the decode attention's E4M3 decoding is checked on every code through a
+  one-slot attention (the output is the V row itself);
+* decode attention and the decode step of the block match the oracle over the
+  dequantized cache within the bf16 attention and block bounds.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8
+from llama_decoder_block_amd import binding, synth
+from metrics import BF16_ULP, max_abs, rel_frobenius, report, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def dev(t):
+    return t.to(DEV)
+
+
+def rows_with_spread(seed, shape, dtype):
+    """Normal rows whose magnitudes span 2**-12 .. 2**12 (per row), one zero
+    row and one row of negative zeros."""
+    x = synth.normal(seed, shape, dtype="f32").to(torch.float64)
+    g = np.random.Generator(np.random.PCG64(seed + 7))
+    e = torch.from_numpy(g.uniform(-12, 12, shape[:-1] + (1,)))
+    x = x * torch.pow(2.0, e)
+    flat = x.reshape(-1, shape[-1])
+    flat[0] = 0.0
+    flat[1] = -0.0
+    return x.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+def upload_cache(kc, vc, ks, vs):
+    """Dense row-major device copies (the layouts the library reads)."""
+    return tuple(dev(torch.from_numpy(np.ascontiguousarray(a))) for a in (kc, vc, ks, vs))
+
+
+def attention_bound(ref, v):
+    vmax = np.abs(v).max()
+    return BF16_ULP * (np.abs(ref) + vmax) + 1e-5
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_append_is_bit_exact(hd, dtype):
+    B, T, nkv, cap = 3, 5, 2, 11
+    k = rows_with_spread(200, (B, T, nkv, hd), dtype)
+    v = rows_with_spread(201, (B, T, nkv, hd), dtype)
+    pos = torch.tensor([[0, 1, 2, 3, 4], [10, 3, 7, 11, -1], [6, 5, 9, 8, 2]], dtype=torch.int32)
+    k8, v8, ks, vs = binding.fp8_cache(B, cap, nkv, hd, DEV)
+    k8.fill_(0x5A)
+    v8.fill_(0x5A)
+    ks.fill_(-1.0)
+    vs.fill_(-1.0)
+    binding.kv_append_fp8(dev(k), dev(v), dev(pos), k8, v8, ks, vs)
+    torch.cuda.synchronize()
+    kc, ksc = fp8.quantize_rows(to64(k))
+    vc, vsc = fp8.quantize_rows(to64(v))
+    gk8, gv8, gks, gvs = k8.cpu().numpy(), v8.cpu().numpy(), ks.cpu().numpy(), vs.cpu().numpy()
+    written = np.zeros((B, cap), dtype=bool)
+    for b in range(B):
+        for t in range(T):
+            p = int(pos[b, t])
+            if not 0 <= p < cap:
+                continue
+            written[b, p] = True
+            np.testing.assert_array_equal(gk8[b, :, p], kc[b, t])
+            np.testing.assert_array_equal(gv8[b, :, p], vc[b, t])
+            np.testing.assert_array_equal(gks[b, :, p], ksc[b, t])
+            np.testing.assert_array_equal(gvs[b, :, p], vsc[b, t])
+    # slots outside the positions (and the out-of-range ones) are untouched
+    assert np.all(gk8.transpose(0, 2, 1, 3)[~written] == 0x5A) and np.all(gv8.transpose(0, 2, 1, 3)[~written] == 0x5A)
+    assert np.all(gks.transpose(0, 2, 1)[~written] == -1.0)
+
+
+def test_decode_of_every_code_through_one_slot_attention():
+    """Query b at position 0 sees only slot 0, so the output is v_scale * E4M3(code)
+    of that slot's V row, exactly (every E4M3 value is a bf16 value); rows
+    hold all 256 codes."""
+    B, nq, nkv, hd, cap = 2, 4, 1, 128, 3
+    k8, v8, ks, vs = binding.fp8_cache(B, cap, nkv, hd, DEV)
+    codes = torch.arange(256, dtype=torch.uint8).reshape(2, 128)
+    v8[:, 0, 0] = dev(codes)
+    k8[:, 0, 0] = 0x38  # [sequence, KV head 0, slot 0]
+    ks.fill_(1.0)
+    vs.fill_(1.0)
+    q = dev(synth.normal(210, (B, 1, nq, hd), dtype="bf16"))
+    pos = dev(torch.zeros(B, dtype=torch.int32))
+    out = binding.gqa_attention_fp8kv(q, k8, v8, ks, vs, pos)
+    torch.cuda.synchronize()
+    want = fp8.e4m3_decode(codes.numpy())
+    got = to64(out[:, 0])  # [B, nq, hd]
+    for h in range(nq):
+        np.testing.assert_array_equal(got[:, h], want)
+
+
+def quantized_cache(seed, B, S, nkv, hd):
+    k = synth.normal(seed, (B, S, nkv, hd), dtype="bf16")
+    v = synth.normal(seed + 1, (B, S, nkv, hd), dtype="bf16")
+    kc, vc, ks, vs = fp8.kv_cache_from_rows(to64(k), to64(v))
+    return kc, vc, ks, vs
+
+
+def poison_unwritten(kc, vc, ks, vs, pos):
+    """Slots after each sequence's position: NaN codes and NaN scales (never read)."""
+    for b, p in enumerate(pos):
+        kc[b, :, p + 1:] = 0xFF
+        vc[b, :, p + 1:] = 0x7F
+        ks[b, :, p + 1:] = np.nan
+        vs[b, :, p + 1:] = np.nan
+
+
+def kernel_used(fn):
+    binding.profile_reset()
+    binding.profile_enable(True)
+    out = fn()
+    torch.cuda.synchronize()
+    names = binding.profile_collect()
+    binding.profile_enable(False)
+    return out, [n for n in names if n.startswith("attention/")]
+
+
+@pytest.mark.parametrize("nq,nkv", [(32, 8), (8, 8), (16, 8), (32, 4), (64, 8)])
+def test_decode_attention_fp8kv(nq, nkv):
+    """Ragged visible lengths over 24 sequences (one workgroup per pair)."""
+    B, S, hd = 24, 700, 128
+    kc, vc, ks, vs = quantized_cache(220, B, S, nkv, hd)
+    lens = [700, 1, 33, 64, 65, 300, 511, 512, 513, 699, 2, 31, 32, 100, 257, 640, 7, 650, 690, 350, 128, 129, 96, 97]
+    pos = np.array([n - 1 for n in lens])
+    kd, vd = fp8.kv_cache_values(kc, ks), fp8.kv_cache_values(vc, vs)
+    poison_unwritten(kc, vc, ks, vs, pos)
+    q = synth.normal(222, (B, 1, nq, hd), dtype="bf16")
+    gk8, gv8, gks, gvs = upload_cache(kc, vc, ks, vs)
+    out, used = kernel_used(lambda: binding.gqa_attention_fp8kv(dev(q), gk8, gv8, gks, gvs,
+                                                                dev(torch.from_numpy(pos.astype(np.int32)))))
+    assert used == ["attention/attn_decode_wg_fp8kv"]
+    ref = oracle.gqa_attention(to64(q), kd, vd, pos[:, None])
+    report(f"decode fp8kv {nq}/{nkv}", out, ref)
+    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, vd))
+
+
+def test_decode_attention_fp8kv_long_context_split():
+    """Two sequences against a 20000-slot cache: chunks over workgroups, merged
+    through the workspace."""
+    B, S, nq, nkv, hd = 2, 20000, 32, 8, 128
+    kc, vc, ks, vs = quantized_cache(230, B, S, nkv, hd)
+    pos = np.array([19999, 8191])
+    kd, vd = fp8.kv_cache_values(kc, ks), fp8.kv_cache_values(vc, vs)
+    poison_unwritten(kc, vc, ks, vs, pos)
+    q = synth.normal(232, (B, 1, nq, hd), dtype="bf16")
+    gk8, gv8, gks, gvs = upload_cache(kc, vc, ks, vs)
+    out, used = kernel_used(lambda: binding.gqa_attention_fp8kv(dev(q), gk8, gv8, gks, gvs,
+                                                                dev(torch.from_numpy(pos.astype(np.int32)))))
+    assert used == ["attention/attn_decode_splitk_fp8kv"]
+    ref = oracle.gqa_attention(to64(q), kd, vd, pos[:, None])
+    report("decode fp8kv split", out, ref)
+    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, vd))
+
+
+@pytest.mark.parametrize("cfg", [dict(d_model=512, n_q=8, n_kv=2, d_ff=1376, kv_cap=67),
+                                 dict(d_model=1024, n_q=16, n_kv=4, d_ff=2816, kv_cap=300)])
+def test_block_decode_fp8kv(cfg):
+    """Decode step of the block against an 8-bit cache filled by the oracle;
+    gates as for the bf16 block (relF and max abs against the storage-point
+    oracle, which here also quantizes the new token's k and v)."""
+    wl = synth.workload("llama3_8b_gqa_decode", batch=5, d_model=cfg["d_model"], n_q=cfg["n_q"],
+                        n_kv=cfg["n_kv"], head_dim=128, d_ff=cfg["d_ff"], decode_pos=cfg["kv_cap"] - 1,
+                        kv_cap=cfg["kv_cap"])
+    inp = synth.make_block_inputs(wl)
+    B, hd, cap = wl.batch, wl.head_dim, cfg["kv_cap"]
+    pos = np.array([0, 5, cap - 1, 33, 17])
+    g = np.random.Generator(np.random.PCG64(240))
+    kprev = oracle.round_bf16(g.standard_normal((B, cap, wl.n_kv, hd)))
+    vprev = oracle.round_bf16(g.standard_normal((B, cap, wl.n_kv, hd)))
+    kc, vc, ks, vs = fp8.kv_cache_from_rows(kprev, vprev)
+    w = {k: to64(t) for k, t in inp.weights.items()}
+    x = to64(inp.x)
+    y_ref, kc_ref, vc_ref, ks_ref, vs_ref = fp8.decode_step_fp8kv(
+        x, w, pos, kc, vc, ks, vs, wl.theta, wl.eps, wl.n_q, wl.n_kv)
+    # the GPU's cache holds NaN codes and scales after each position (never read)
+    pk, pv, pks, pvs = kc.copy(), vc.copy(), ks.copy(), vs.copy()
+    poison_unwritten(pk, pv, pks, pvs, pos)
+    gk8, gv8, gks, gvs = upload_cache(pk, pv, pks, pvs)
+    wd = {k: dev(t) for k, t in inp.weights.items()}
+    y = binding.block_forward_fp8kv(dev(inp.x), wd, dev(torch.from_numpy(pos.astype(np.int32))), wl.n_q, wl.n_kv,
+                                    wl.theta, wl.eps, gk8, gv8, gks, gvs)
+    torch.cuda.synchronize()
+    report(f"block decode fp8kv d{cfg['d_model']}", y, y_ref)
+    report(f"block decode fp8kv d{cfg['d_model']} delta y-x", to64(y) - x, y_ref - x)
+    assert rel_frobenius(y, y_ref) <= 1e-2
+    assert max_abs(y, y_ref) <= 5e-2
+    # the sublayer contributions themselves (x dominates y)
+    assert rel_frobenius(to64(y) - x, y_ref - x) <= 1e-2
+    # the new token's cache rows: the GPU quantized its own k and v, which may
+    # differ from the oracle's by bf16 rounding flips; compare the stored values
+    got_k = fp8.kv_cache_values(gk8.cpu().numpy(), gks.cpu().numpy())
+    want_k = fp8.kv_cache_values(kc_ref, ks_ref)
+    for b, p in enumerate(pos):
+        d = np.abs(got_k[b, p] - want_k[b, p])
+        assert np.all(d <= np.abs(want_k[b, p]) / 8 + 2.0 ** -9 * np.abs(want_k[b, p]).max() + 1e-6)
+        # the other slots are untouched
+        keep = np.arange(p)
+        np.testing.assert_array_equal(gk8.cpu().numpy()[b][:, keep], kc[b][:, keep])

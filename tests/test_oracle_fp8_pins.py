@@ -112,3 +112,36 @@ def test_grid_values_with_unit_scale_are_stored_exactly():
 def test_rejects_values_fp32_cannot_hold():
     with pytest.raises(ValueError):
         fp8.quantize_rows(np.array([[1.0 + 2.0 ** -40]]))
+
+
+def test_decode_step_fp8kv_reduces_to_plain_decode_for_zero_new_rows():
+    # with W_k = W_v = 0 the new token's k and v are exactly zero, so its cache
+    # row is scale 0 / codes 0 and the step equals the plain decode step over
+    # the dequantized cache; the other slots are left as they were
+    g = rng(7)
+    d, nq, nkv, hd, dff, B, S = 64, 4, 2, 128, 96, 2, 9
+    w = {"attn_norm": 1.0 + 0.1 * g.standard_normal(d), "wq": 0.05 * g.standard_normal((nq * hd, d)),
+         "wk": np.zeros((nkv * hd, d)), "wv": np.zeros((nkv * hd, d)),
+         "wo": 0.05 * g.standard_normal((d, nq * hd)), "ffn_norm": 1.0 + 0.1 * g.standard_normal(d),
+         "w_gate": 0.05 * g.standard_normal((dff, d)), "w_up": 0.05 * g.standard_normal((dff, d)),
+         "w_down": 0.05 * g.standard_normal((d, dff))}
+    # cache rows on the E4M3 grid with maximum 448 (scale 1), so that the
+    # dequantized cache is also a bf16 tensor and the plain step's bf16
+    # storage point leaves it unchanged
+    grid = fp8.e4m3_decode(np.arange(0x00, 0x7F, dtype=np.uint8)) / 64.0
+    k = g.choice(grid, size=(B, S, nkv, hd)) * g.choice([-1.0, 1.0], size=(B, S, nkv, hd))
+    v = g.choice(grid, size=(B, S, nkv, hd)) * g.choice([-1.0, 1.0], size=(B, S, nkv, hd))
+    k[..., 0] = v[..., 1] = 7.0
+    kc, vc, ks, vs = fp8.kv_cache_from_rows(k, v)
+    assert np.array_equal(fp8.kv_cache_values(kc, ks), k)
+    x = g.standard_normal((B, 1, d))
+    pos = [3, 8]
+    y, kc2, vc2, ks2, vs2 = fp8.decode_step_fp8kv(x, w, pos, kc, vc, ks, vs, 1e4, 1e-5, nq, nkv)
+    kd, vd = fp8.kv_cache_values(kc, ks), fp8.kv_cache_values(vc, vs)
+    y_plain = oracle.decode_step(x, w, pos, kd, vd, 1e4, 1e-5, nq, nkv, bf16_storage=True)[0]
+    assert np.array_equal(y, y_plain)
+    for b, p in enumerate(pos):
+        assert np.all(kc2[b, :, p] == 0) and np.all(vc2[b, :, p] == 0)
+        assert np.all(ks2[b, :, p] == 0) and np.all(vs2[b, :, p] == 0)
+        keep = [j for j in range(S) if j != p]
+        assert np.array_equal(kc2[b][:, keep], kc[b][:, keep]) and np.array_equal(ks2[b][:, keep], ks[b][:, keep])

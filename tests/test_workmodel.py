@@ -53,3 +53,12 @@ def test_step_work_sums_to_block_totals():
     # decode: the weights dominate the GEMM steps' bytes (activations add ~2%)
     wbytes = sum(dec[k][1] for k in ("qkv_rope", "o_resid", "gate_up_silu", "down_resid"))
     assert wm.decode_weight_bytes(L3_8B) < wbytes < 1.03 * wm.decode_weight_bytes(L3_8B)
+
+
+def test_fp8_kv_bytes_halve_the_cache_plus_row_scales():
+    # [LA] §4 memory formula with bytes_per_elem = 1, plus 4 bytes per cached row
+    b16 = wm.decode_attention_bytes(L3_8B, 64, 4097)
+    b8 = wm.decode_attention_bytes_fp8kv(L3_8B, 64, 4097)
+    assert b8 == b16 // 2 + 64 * 4097 * 2 * 8 * 4
+    w = wm.step_work(L3_8B, 64, 1, attend_len=4097, kv_bytes=wm.FP8KV_BYTES_PER_ELEM)
+    assert w["attention"][1] == b8
