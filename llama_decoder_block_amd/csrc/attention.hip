@@ -1081,6 +1081,10 @@ int d3_blocks_per_cu(int nw) {
 // or 16: more concurrent streams than that cost HBM page locality, fewer
 // leave bandwidth idle.
 constexpr int kDecWavesPerCu = 6;
+// The 8-bit cache's rows are half as long and each wavefront keeps two steps
+// in flight; its sweep on the same workload: 4 / 6 / 8 / 10 / 12 / 16 per CU
+// gave 131 / 115 / 109 / 121 / 119 / 120 us.
+constexpr int kDecWavesPerCuFp8 = 8;
 
 // Wavefronts per (sequence, KV head) workgroup of attn_decode3_kernel: close
 // to the target count, all workgroups resident in one round, within LDS.
@@ -1098,7 +1102,7 @@ template <int R, bool KV8>
 hipError_t launch_decode_bf16(const AttnArgs& a, void* ws, hipStream_t s, const char** kernel_name) {
   constexpr int HD = 128;
   const int64_t pairs = static_cast<int64_t>(a.B) * a.nkv;
-  const int64_t target = static_cast<int64_t>(device_cus()) * kDecWavesPerCu;
+  const int64_t target = static_cast<int64_t>(device_cus()) * (KV8 ? kDecWavesPerCuFp8 : kDecWavesPerCu);
   const int nw = d3_pick_waves<R, KV8>(pairs, target);
   if (pairs * nw * 2 >= target) {
     // one workgroup per (sequence, KV head) reaches at least half the target
