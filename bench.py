@@ -224,6 +224,50 @@ def bench_decode_fp8kv(wd, dev, args):
     return out
 
 
+def bench_paged_attention(wd, dev, args, page_size=64):
+    """Decode attention alone over the same bf16 history held in a paged cache
+    (pages of 64 slots, page order shuffled), against the contiguous cache's
+    kernel on the same data; the last-level cache is flushed between calls."""
+    inp = synth.make_block_inputs(wd)
+    B, cap, nkv, hd, nq = wd.batch, wd.kv_cap, wd.n_kv, wd.head_dim, wd.n_q
+    max_pages = -(-cap // page_size)
+    n_pages = B * max_pages
+    g = torch.Generator().manual_seed(4000 + 12)
+    table = torch.randperm(n_pages, generator=g).to(torch.int32).reshape(B, max_pages)
+    kc = torch.zeros(B, max_pages * page_size, nkv, hd, dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    kc[:, :cap], vc[:, :cap] = inp.k_cache, inp.v_cache
+    kpool = torch.empty(n_pages, page_size, nkv, hd, dtype=torch.bfloat16, device=dev)
+    vpool = torch.empty_like(kpool)
+    flat = table.reshape(-1).to(dev).long()
+    kpool[flat] = kc.reshape(n_pages, page_size, nkv, hd).to(dev)
+    vpool[flat] = vc.reshape(n_pages, page_size, nkv, hd).to(dev)
+    del kc, vc
+    q = synth.normal(4013, (B, 1, nq, hd), dtype="bf16").to(dev)
+    pos = inp.positions.reshape(-1).to(dev)
+    tab = table.to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(binding.lib().llama_gqa_attention_paged_workspace_bytes(B, max_pages, page_size, nq, nkv, hd),
+                     dtype=torch.uint8, device=dev)
+    scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    _, _, dk = time_steps(lambda: binding.gqa_attention_paged(q, kpool, vpool, tab, pos, out=out, workspace=ws),
+                          args.decode_steps, args.warmup, flush=lambda: scratch.sum())
+    name = DECODE_ATTN + "_paged"
+    n_at, ms_at = dk.get(name, (0, 0.0))
+    at_avg = ms_at / max(n_at, 1)
+    at_bytes = wm.decode_attention_bytes(shape_of(wd), B, wd.decode_pos + 1)
+    at_gbs = at_bytes / (at_avg * 1e-3) / 1e9 if n_at else 0.0
+    log(f"[bench] decode attention, paged cache (pages of {page_size} slots, shuffled): {at_avg * 1e3:.1f} us = "
+        f"{at_gbs:.0f} GB/s")
+    del scratch, kpool, vpool
+    torch.cuda.empty_cache()
+    return {"workload": f"{DECODE} attention over a paged bf16 cache: pages of {page_size} slots in a pool "
+                        f"[{n_pages},{page_size},{nkv},{hd}], block table [{B},{max_pages}] in shuffled order",
+            "kernel": name, "bound": "hbm", "avg_us": round(at_avg * 1e3, 2), "bytes": at_bytes,
+            "achieved": round(at_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(at_gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +374,7 @@ def main():
         del dstep
         torch.cuda.empty_cache()
         decode["fp8kv"] = bench_decode_fp8kv(wd, dev, args)
+        decode["paged_attention"] = bench_paged_attention(wd, dev, args)
 
     cpu = None
     if not args.no_cpu_baseline:

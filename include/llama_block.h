@@ -221,6 +221,40 @@ size_t llama_block_forward_fp8kv_workspace_bytes(int32_t batch, int32_t d_model,
                                                  int32_t n_kv_heads, int32_t head_dim, int32_t d_ff,
                                                  int32_t kv_cap, int rdtype);
 
+/* Paged KV cache ([LA] "Troubleshooting Common Deployment Faults", item 3:
+ * a paged cache allocates KV history in fixed-size pages of a shared pool
+ * instead of one contiguous region per sequence).  Pools k_pages, v_pages:
+ * bf16 [n_pages, page_size, n_kv, hd] (a page holds page_size consecutive
+ * slots of one sequence, token-major like the contiguous cache);
+ * block_table: int32 [batch, max_pages]; slot j of sequence b is row
+ * j % page_size of page block_table[b*max_pages + j/page_size].  page_size
+ * must be a multiple of 32.  Table entries for visible slots must lie in
+ * [0, n_pages); the kernels clamp other entries into the pool (so a bad table
+ * reads wrong rows but stays inside memory). */
+
+/* Copies the bf16 rows k, v [batch, seq_len, n_kv, hd] into the pools at slot
+ * positions[b, t] (tokens whose slot lies outside the table, or whose page
+ * entry lies outside [0, n_pages), are skipped).  head_dim % 8 == 0, <= 256. */
+int llama_kv_append_paged(const void* k, const void* v, const int32_t* positions,
+                          const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                          int32_t batch, int32_t seq_len, int32_t n_kv_heads, int32_t head_dim,
+                          void* k_pages, void* v_pages, int64_t n_pages, void* stream);
+
+/* Decode attention (one bf16 query token per sequence, the operation of
+ * llama_gqa_attention with q_len == 1) over a paged cache.  q, out: bf16
+ * [batch, n_q, hd]; positions: [batch] (query b sees slots 0..positions[b],
+ * each < max_pages * page_size).  head_dim must be 128 and n_q/n_kv one of
+ * 1, 2, 4, 8.  workspace: at least
+ * llama_gqa_attention_paged_workspace_bytes(...) bytes. */
+int llama_gqa_attention_paged(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                              int64_t n_pages, void* out, const int32_t* positions, int32_t batch,
+                              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                              void* workspace, size_t ws_bytes, void* stream);
+size_t llama_gqa_attention_paged_workspace_bytes(int32_t batch, int32_t max_pages, int32_t page_size,
+                                                 int32_t n_q_heads, int32_t n_kv_heads,
+                                                 int32_t head_dim);
+
 /* Host-only helpers. */
 const char* llama_last_error(void);    /* thread-local text of the last failure ("" if none) */
 const char* llama_status_string(int status);

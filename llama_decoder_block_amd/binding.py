@@ -24,7 +24,8 @@ FUNCTIONS = [
     "llama_version", "llama_profile_enable", "llama_profile_reset", "llama_profile_collect",
     "llama_profile_query", "llama_profile_names", "llama_kv_append_fp8", "llama_gqa_attention_fp8kv",
     "llama_gqa_attention_fp8kv_workspace_bytes", "llama_block_forward_fp8kv",
-    "llama_block_forward_fp8kv_workspace_bytes",
+    "llama_block_forward_fp8kv_workspace_bytes", "llama_kv_append_paged", "llama_gqa_attention_paged",
+    "llama_gqa_attention_paged_workspace_bytes",
 ]
 
 
@@ -85,6 +86,11 @@ def lib():
                                        _i32, _i32, _i32, _i32, _i32, _i32, _f64, _f64, _int, _vp, _sz, _vp],
                                       _int),
         "llama_block_forward_fp8kv_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _int], _sz),
+        "llama_kv_append_paged": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _vp],
+                                  _int),
+        "llama_gqa_attention_paged": ([_vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _vp,
+                                       _sz, _vp], _int),
+        "llama_gqa_attention_paged_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -264,6 +270,31 @@ def block_forward_fp8kv(x, w, positions, n_q_heads, n_kv_heads, rope_theta, eps,
 
 def block_fp8kv_workspace_bytes(batch, d, nq, nkv, hd, dff, kv_cap, rdtype):
     return lib().llama_block_forward_fp8kv_workspace_bytes(batch, d, nq, nkv, hd, dff, kv_cap, rdtype)
+
+
+# --- paged KV cache ------------------------------------------------------------
+def kv_append_paged(k, v, positions, block_table, k_pages, v_pages):
+    """Copy k, v [B, T, n_kv, hd] bf16 into the page pools [n_pages, P, n_kv, hd]
+    at slots positions [B, T] through block_table [B, max_pages]."""
+    B, T, nkv, hd = k.shape
+    _check(lib().llama_kv_append_paged(_p(k), _p(v), _p(positions), _p(block_table), block_table.shape[1],
+                                       k_pages.shape[1], B, T, nkv, hd, _p(k_pages), _p(v_pages), k_pages.shape[0],
+                                       _stream()))
+
+
+def gqa_attention_paged(q, k_pages, v_pages, block_table, positions, out=None, workspace=None):
+    """Decode attention: q [B, 1, n_q, hd] bf16 (or [B, n_q, hd]) over the page pools."""
+    B, nq, hd = q.shape[0], q.shape[-2], q.shape[-1]
+    n_pages, P, nkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    max_pages = block_table.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    L = lib()
+    need = L.llama_gqa_attention_paged_workspace_bytes(B, max_pages, P, nq, nkv, hd)
+    ws, nbytes = _workspace(need, q.device, workspace)
+    _check(L.llama_gqa_attention_paged(_p(q), _p(k_pages), _p(v_pages), _p(block_table), max_pages, P, n_pages,
+                                       _p(out), _p(positions), B, nq, nkv, hd, _p(ws), nbytes, _stream()))
+    return out
 
 
 # --- kernel timing -----------------------------------------------------------

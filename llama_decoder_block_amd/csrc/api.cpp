@@ -595,7 +595,7 @@ int check_fp8_attention_shape(int32_t n_q_heads, int32_t n_kv_heads, int32_t hea
   if (st != LLAMA_OK) return st;
   const int r = n_q_heads / n_kv_heads;
   if (head_dim != 128 || (r != 1 && r != 2 && r != 4 && r != 8))
-    return fail(LLAMA_ERR_UNSUPPORTED, "the 8-bit cache attention needs head_dim 128 and n_q/n_kv in {1,2,4,8}");
+    return fail(LLAMA_ERR_UNSUPPORTED, "this decode attention needs head_dim 128 and n_q/n_kv in {1,2,4,8}");
   return LLAMA_OK;
 }
 
@@ -661,6 +661,90 @@ int llama_block_forward_fp8kv(const void* x, void* y, const llama_block_weights*
   return run_block(x, y, w, positions, nullptr, nullptr, kv_cap, batch, 1, d_model, n_q_heads, n_kv_heads,
                    head_dim, d_ff, rope_theta, eps, DType::BF16, static_cast<DType>(rdtype), workspace, ws_bytes,
                    static_cast<hipStream_t>(stream), &c8);
+}
+
+// ---------------------------------------------------------------------------
+// paged KV cache
+// ---------------------------------------------------------------------------
+namespace {
+
+int check_paged(const void* kp, const void* vp, const int32_t* table, int32_t max_pages, int32_t page_size,
+                int64_t n_pages) {
+  if (!kp || !vp || !table) return fail(LLAMA_ERR_INVALID_ARGUMENT, "page pools and block table must be non-null");
+  if (max_pages <= 0 || page_size <= 0 || n_pages <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "max_pages, page_size and n_pages must be > 0");
+  if (page_size % 32 != 0)
+    return fail(LLAMA_ERR_UNSUPPORTED, "page_size (%d) must be a multiple of 32", page_size);
+  if (static_cast<int64_t>(max_pages) * page_size > 0x7fffffff)
+    return fail(LLAMA_ERR_UNSUPPORTED, "max_pages * page_size too large");
+  for (const void* p : std::initializer_list<const void*>{kp, vp, static_cast<const void*>(table)})
+    if (!aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+int llama_kv_append_paged(const void* k, const void* v, const int32_t* positions, const int32_t* block_table,
+                          int32_t max_pages, int32_t page_size, int32_t batch, int32_t seq_len, int32_t n_kv_heads,
+                          int32_t head_dim, void* k_pages, void* v_pages, int64_t n_pages, void* stream) {
+  if (batch < 0 || seq_len < 0 || n_kv_heads <= 0 || head_dim <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "batch, seq_len must be >= 0; n_kv_heads, head_dim > 0");
+  if (head_dim % 8 != 0 || head_dim > 256)
+    return fail(LLAMA_ERR_UNSUPPORTED, "head_dim (%d) must be a multiple of 8 and at most 256", head_dim);
+  int st = check_paged(k_pages, v_pages, block_table, max_pages, page_size, n_pages);
+  if (st != LLAMA_OK) return st;
+  const int64_t n = static_cast<int64_t>(batch) * seq_len;
+  if (n == 0) return ok();
+  if (!k || !v || !positions) return fail(LLAMA_ERR_INVALID_ARGUMENT, "k, v and positions must be non-null");
+  if (!aligned16(k) || !aligned16(v)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("kv_append_paged", s, [&](const char** name) {
+    *name = "kv_append_paged";
+    return lb::launch_kv_append_paged(k, v, positions, n, seq_len, n_kv_heads, head_dim, block_table, max_pages,
+                                      page_size, n_pages, k_pages, v_pages, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_kv_append_paged");
+  return ok();
+}
+
+size_t llama_gqa_attention_paged_workspace_bytes(int32_t batch, int32_t max_pages, int32_t page_size,
+                                                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
+  if (batch <= 0 || max_pages <= 0 || page_size <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim != 128)
+    return 0;
+  const int64_t S = static_cast<int64_t>(max_pages) * page_size;
+  if (S > 0x7fffffff) return 0;
+  return lb::attention_paged_workspace_bytes(batch, static_cast<int>(S), n_q_heads);
+}
+
+int llama_gqa_attention_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                              int32_t max_pages, int32_t page_size, int64_t n_pages, void* out,
+                              const int32_t* positions, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                              int32_t head_dim, void* workspace, size_t ws_bytes, void* stream) {
+  if (batch < 0) return fail(LLAMA_ERR_INVALID_ARGUMENT, "batch must be >= 0");
+  int st = check_fp8_attention_shape(n_q_heads, n_kv_heads, head_dim);
+  if (st != LLAMA_OK) return st;
+  st = check_paged(k_pages, v_pages, block_table, max_pages, page_size, n_pages);
+  if (st != LLAMA_OK) return st;
+  if (batch == 0) return ok();
+  if (!q || !out || !positions) return fail(LLAMA_ERR_INVALID_ARGUMENT, "q, out and positions must be non-null");
+  if (out == q) return fail(LLAMA_ERR_INVALID_ARGUMENT, "out must not alias q");
+  for (const void* p : std::initializer_list<const void*>{q, static_cast<const void*>(out), workspace})
+    if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  const size_t need = llama_gqa_attention_paged_workspace_bytes(batch, max_pages, page_size, n_q_heads, n_kv_heads,
+                                                                head_dim);
+  if (ws_bytes < need || !workspace)
+    return fail(LLAMA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  lb::AttnArgs a{};
+  a.q = q; a.k = k_pages; a.v = v_pages; a.out = out; a.positions = positions;
+  a.B = batch; a.Tq = 1; a.S = max_pages * page_size; a.nq = n_q_heads; a.nkv = n_kv_heads; a.hd = head_dim;
+  a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(head_dim)));
+  a.block_table = block_table; a.max_pages = max_pages; a.page_size = page_size; a.n_pages = n_pages;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("attention", s, [&](const char** name) {
+    return lb::launch_attention_paged(a, workspace, ws_bytes, s, name);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_gqa_attention_paged");
+  return ok();
 }
 
 // ---------------------------------------------------------------------------

@@ -674,6 +674,21 @@ __device__ __forceinline__ void fp8x8_to_f32(uint32_t d0, uint32_t d1, float v[8
   v[4] = c[0]; v[5] = c[1]; v[6] = e[0]; v[7] = e[1];
 }
 
+// Paged cache: slot j of sequence b is row j % P of page table[j / P] in a
+// pool [n_pages, P, n_kv, hd].  P is a multiple of the 32-slot step and steps
+// start on multiples of 32, so one table entry serves a whole step; entries
+// outside [0, n_pages) are clamped into the pool (a valid table never has
+// them for visible slots; the clamp only keeps a bad table inside memory).
+// The loops read the next step's table entry before this step's loads, so
+// the indirection adds no dependent round trip.
+__device__ __forceinline__ void dec_load_paged(DecRegs& r, const bf16_t* kpool, const bf16_t* vpool, int page,
+                                               int P, int64_t n_pages, int64_t kvrow, int js, int jend, int col,
+                                               int grp) {
+  const int64_t pg = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
+  const int64_t base = (pg * P + (js % P)) * kvrow;
+  dec_load(r, kpool + base, vpool + base, kvrow, 0, jend - js, col, grp);
+}
+
 template <int R>
 struct DecState {
   static constexpr int RP = R > 4 ? R : 4;
@@ -786,7 +801,7 @@ struct DecState {
   }
 };
 
-template <int R, bool KV8>
+template <int R, bool KV8, bool PAGED = false>
 __global__ void __launch_bounds__(256)
 attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__ part_o,
                     float* __restrict__ part_ml) {
@@ -809,9 +824,11 @@ attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__
   // K/V rows of (b, g): bf16 elements, or E4M3 codes (one byte each) plus
   // the fp32 row scales [n_kv][S] of the sequence
   const int64_t kvrow = static_cast<int64_t>(a.nkv) * HD;
-  const int64_t kvoff = (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
+  // (paged: the pool base at KV head g; the table picks the page per step)
+  const int64_t kvoff = PAGED ? static_cast<int64_t>(g) * HD : (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
   const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + kvoff;
   const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + kvoff;
+  const int32_t* table = PAGED ? a.block_table + static_cast<int64_t>(b) * a.max_pages : nullptr;
   const int col = lane & 15, grp = lane >> 4;
   Dec8Src src8;
   if constexpr (KV8) {
@@ -850,9 +867,16 @@ attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__
       st.step(rb, qf, c, js + SUB, jend, col, grp, s_p[w], s_alpha[w]);
     }
   } else {
+    int page = PAGED && j0 <= jend ? table[j0 / a.page_size] : 0;
     for (int js = j0; js <= jend; js += SUB) {
       DecRegs rr;
-      dec_load(rr, kbase, vbase, kvrow, js, jend, col, grp);
+      if constexpr (PAGED) {
+        const int next = table[min(js + SUB, jend) / a.page_size];
+        dec_load_paged(rr, kbase, vbase, page, a.page_size, a.n_pages, kvrow, js, jend, col, grp);
+        page = next;
+      } else {
+        dec_load(rr, kbase, vbase, kvrow, js, jend, col, grp);
+      }
       st.step(rr, qf, c, js, jend, col, grp, s_p[w], s_alpha[w]);
     }
   }
@@ -891,7 +915,7 @@ attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__
 // At most 16 wavefronts per workgroup (8 for R = 8, whose accumulators need
 // more than the 128 registers a 16-wavefront workgroup leaves per lane, and
 // for the 8-bit cache, whose two steps of registers in flight need more too).
-template <int R, bool KV8>
+template <int R, bool KV8, bool PAGED = false>
 __global__ void __launch_bounds__(R >= 8 || KV8 ? 512 : 1024)
 attn_decode3_kernel(AttnArgs a) {
   constexpr int HD = 128, SUB = kDSub;
@@ -912,9 +936,11 @@ attn_decode3_kernel(AttnArgs a) {
   // K/V rows of (b, g): bf16 elements, or E4M3 codes (one byte each) plus
   // the fp32 row scales [n_kv][S] of the sequence
   const int64_t kvrow = static_cast<int64_t>(a.nkv) * HD;
-  const int64_t kvoff = (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
+  // (paged: the pool base at KV head g; the table picks the page per step)
+  const int64_t kvoff = PAGED ? static_cast<int64_t>(g) * HD : (static_cast<int64_t>(b) * a.S * a.nkv + g) * HD;
   const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + kvoff;
   const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + kvoff;
+  const int32_t* table = PAGED ? a.block_table + static_cast<int64_t>(b) * a.max_pages : nullptr;
   const int col = lane & 15, grp = lane >> 4;
   Dec8Src src8;
   if constexpr (KV8) {
@@ -952,9 +978,16 @@ attn_decode3_kernel(AttnArgs a) {
       st.step(rb, qf, c, js + SUB, jend, col, grp, s_p[w], my_alpha);
     }
   } else {
+    int page = PAGED && j0 <= jend ? table[j0 / a.page_size] : 0;
     for (int js = j0; js <= jend; js += SUB) {
       DecRegs rr;
-      dec_load(rr, kbase, vbase, kvrow, js, jend, col, grp);
+      if constexpr (PAGED) {
+        const int next = table[min(js + SUB, jend) / a.page_size];
+        dec_load_paged(rr, kbase, vbase, page, a.page_size, a.n_pages, kvrow, js, jend, col, grp);
+        page = next;
+      } else {
+        dec_load(rr, kbase, vbase, kvrow, js, jend, col, grp);
+      }
       st.step(rr, qf, c, js, jend, col, grp, s_p[w], my_alpha);
     }
   }
@@ -1055,7 +1088,7 @@ constexpr int d3_max_waves() { return R >= 8 || KV8 ? 8 : 16; }
 
 // Workgroups of attn_decode3_kernel<R> with nw wavefronts that one CU holds
 // at once (register, LDS and wave-slot limits), cached per device.
-template <int R, bool KV8>
+template <int R, bool KV8, bool PAGED>
 int d3_blocks_per_cu(int nw) {
   static thread_local int cached_dev = -1;
   static thread_local int cache[17];
@@ -1067,7 +1100,7 @@ int d3_blocks_per_cu(int nw) {
   }
   if (cache[nw] < 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_decode3_kernel<R, KV8>, 64 * nw,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_decode3_kernel<R, KV8, PAGED>, 64 * nw,
                                                      decode3_lds_bytes(R, nw)) != hipSuccess)
       n = 0;
     cache[nw] = n;
@@ -1088,39 +1121,40 @@ constexpr int kDecWavesPerCuFp8 = 8;
 
 // Wavefronts per (sequence, KV head) workgroup of attn_decode3_kernel: close
 // to the target count, all workgroups resident in one round, within LDS.
-template <int R, bool KV8>
+template <int R, bool KV8, bool PAGED>
 int d3_pick_waves(int64_t pairs, int64_t target) {
   const int cus = device_cus();
   int nw = static_cast<int>(std::min<int64_t>(d3_max_waves<R, KV8>(), std::max<int64_t>(1, (target + pairs / 2) / pairs)));
   while (nw > 1 && (decode3_lds_bytes(R, nw) > kD3MaxLds ||
-                    pairs > static_cast<int64_t>(d3_blocks_per_cu<R, KV8>(nw)) * cus))
+                    pairs > static_cast<int64_t>(d3_blocks_per_cu<R, KV8, PAGED>(nw)) * cus))
     --nw;
   return nw;
 }
 
-template <int R, bool KV8>
+template <int R, bool KV8, bool PAGED = false>
 hipError_t launch_decode_bf16(const AttnArgs& a, void* ws, hipStream_t s, const char** kernel_name) {
   constexpr int HD = 128;
   const int64_t pairs = static_cast<int64_t>(a.B) * a.nkv;
   const int64_t target = static_cast<int64_t>(device_cus()) * (KV8 ? kDecWavesPerCuFp8 : kDecWavesPerCu);
-  const int nw = d3_pick_waves<R, KV8>(pairs, target);
+  const int nw = d3_pick_waves<R, KV8, PAGED>(pairs, target);
   if (pairs * nw * 2 >= target) {
     // one workgroup per (sequence, KV head) reaches at least half the target
-    if (kernel_name) *kernel_name = KV8 ? "attn_decode_wg_fp8kv" : "attn_decode_wg";
-    hipLaunchKernelGGL((attn_decode3_kernel<R, KV8>), dim3(static_cast<unsigned>(pairs)), dim3(64 * nw),
+    if (kernel_name) *kernel_name = KV8 ? "attn_decode_wg_fp8kv" : PAGED ? "attn_decode_wg_paged" : "attn_decode_wg";
+    hipLaunchKernelGGL((attn_decode3_kernel<R, KV8, PAGED>), dim3(static_cast<unsigned>(pairs)), dim3(64 * nw),
                        decode3_lds_bytes(R, nw), s, a);
     return hipGetLastError();
   }
   // few pairs (long contexts, small batches): split the slots of each pair
   // into chunks across wavefronts of their own, then merge the partials
-  if (kernel_name) *kernel_name = KV8 ? "attn_decode_splitk_fp8kv" : "attn_decode_splitk";
+  if (kernel_name)
+    *kernel_name = KV8 ? "attn_decode_splitk_fp8kv" : PAGED ? "attn_decode_splitk_paged" : "attn_decode_splitk";
   const int64_t want = std::max<int64_t>(1, target / pairs);
   int chunk = static_cast<int>(((a.S + want - 1) / want + kDSub - 1) / kDSub * kDSub);
   chunk = std::max(chunk, kDChunk);  // never more chunks than the workspace holds
   const int nch = (a.S + chunk - 1) / chunk;
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + static_cast<int64_t>(a.B) * a.nq * nch * HD;
-  hipLaunchKernelGGL((attn_decode2_kernel<R, KV8>), dim3(static_cast<unsigned>((pairs * nch + 3) / 4)), dim3(256), 0, s,
+  hipLaunchKernelGGL((attn_decode2_kernel<R, KV8, PAGED>), dim3(static_cast<unsigned>((pairs * nch + 3) / 4)), dim3(256), 0, s,
                      a, nch, chunk, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1205,6 +1239,26 @@ hipError_t launch_attention_fp8kv(const AttnArgs& a, void* ws, size_t ws_bytes, 
     case 2: return launch_decode_bf16<2, true>(a, ws, s, kernel_name);
     case 4: return launch_decode_bf16<4, true>(a, ws, s, kernel_name);
     case 8: return launch_decode_bf16<8, true>(a, ws, s, kernel_name);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+size_t attention_paged_workspace_bytes(int B, int S, int nq) {
+  return static_cast<size_t>(B) * nq * decode_chunks(S) * (128 + 2) * sizeof(float);
+}
+
+hipError_t launch_attention_paged(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
+                                  const char** kernel_name) {
+  if (a.B == 0) return hipSuccess;
+  if (a.Tq != 1 || a.hd != 128 || !a.block_table || a.page_size <= 0 || a.page_size % kDSub != 0 ||
+      a.n_pages <= 0)
+    return hipErrorInvalidValue;
+  if (ws_bytes < attention_paged_workspace_bytes(a.B, a.S, a.nq)) return hipErrorInvalidValue;
+  switch (a.nq / a.nkv) {
+    case 1: return launch_decode_bf16<1, false, true>(a, ws, s, kernel_name);
+    case 2: return launch_decode_bf16<2, false, true>(a, ws, s, kernel_name);
+    case 4: return launch_decode_bf16<4, false, true>(a, ws, s, kernel_name);
+    case 8: return launch_decode_bf16<8, false, true>(a, ws, s, kernel_name);
     default: return hipErrorInvalidValue;
   }
 }

@@ -300,6 +300,12 @@ struct AttnArgs {
   float scale;         // 1/sqrt(hd)
   const float* k_scale;  // 8-bit cache only: fp32 row scales [B, nkv, S] of k and v
   const float* v_scale;
+  // paged cache only: k, v are page pools [n_pages, page_size, nkv, hd] and
+  // slot j of sequence b is row j % page_size of page
+  // block_table[b * max_pages + j / page_size]; S = max_pages * page_size
+  const int32_t* block_table;
+  int max_pages, page_size;
+  int64_t n_pages;
 };
 
 size_t attention_workspace_bytes(DType dt, int B, int Tq, int S, int nq, int nkv, int hd);
@@ -317,6 +323,19 @@ hipError_t launch_attention(DType dt, const AttnArgs& a, void* ws, size_t ws_byt
 size_t attention_fp8kv_workspace_bytes(int B, int S, int nq, int nkv);
 hipError_t launch_attention_fp8kv(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
                                   const char** kernel_name);
+
+// Decode attention (Tq == 1, hd == 128, bf16) over a paged cache (the
+// block_table / max_pages / page_size / n_pages fields; page_size % 32 == 0).
+size_t attention_paged_workspace_bytes(int B, int S, int nq);
+hipError_t launch_attention_paged(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
+                                  const char** kernel_name);
+
+// Copies rows k, v [n_tokens, nkv, hd] (bf16) to the paged pools at slot
+// positions[n] of sequence n / seq_len (tokens whose slot or page is outside
+// the table / pool are skipped).
+hipError_t launch_kv_append_paged(const void* k, const void* v, const int32_t* positions, int64_t n_tokens,
+                                  int seq_len, int nkv, int hd, const int32_t* block_table, int max_pages,
+                                  int page_size, int64_t n_pages, void* k_pool, void* v_pool, hipStream_t s);
 
 // Quantizes rows k, v [n_tokens, nkv, hd] (dtype dt) and stores them at slot
 // positions[n] of sequence n / seq_len (tokens whose slot is outside

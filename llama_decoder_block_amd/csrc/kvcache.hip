@@ -12,6 +12,10 @@
 // elements; the row maximum is a wavefront reduction and the encoding is done
 // on the fp32 bit pattern (exponent and mantissa fields), not with a
 // conversion instruction, so its rounding is exactly the rule above.
+// kv_append_paged_kernel: the bf16 rows of new tokens into a paged cache
+// (the same page's slots are consecutive; the block table maps a sequence's
+// slot range to pages of a shared pool, the remedy the same troubleshooting
+// item names for fragmented contiguous caches).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -105,7 +109,41 @@ hipError_t launch_append_t(const void* k, const void* v, const int32_t* position
   return hipGetLastError();
 }
 
+// Paged bf16 cache writer: one thread per 16 bytes of a (token, KV head) row.
+__global__ void __launch_bounds__(256)
+kv_append_paged_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v, const int32_t* __restrict__ positions,
+                       int64_t n_tokens, int seq_len, int nkv, int chunks, const int32_t* __restrict__ table,
+                       int max_pages, int page_size, int64_t n_pages, u32x4* __restrict__ kp, u32x4* __restrict__ vp) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;  // (token, head, chunk)
+  const int64_t row_chunks = static_cast<int64_t>(nkv) * chunks;
+  if (i >= n_tokens * row_chunks) return;
+  const int64_t n = i / row_chunks;
+  const int64_t within = i - n * row_chunks;  // head * chunks + chunk
+  const int pos = positions[n];
+  const int64_t b = n / seq_len;
+  if (pos < 0 || pos >= max_pages * page_size) return;
+  const int64_t pg = table[b * max_pages + pos / page_size];
+  if (pg < 0 || pg >= n_pages) return;
+  const int64_t dst = ((pg * page_size + pos % page_size) * nkv) * chunks + within;
+  kp[dst] = k[i];
+  vp[dst] = v[i];
+}
+
 }  // namespace
+
+hipError_t launch_kv_append_paged(const void* k, const void* v, const int32_t* positions, int64_t n_tokens,
+                                  int seq_len, int nkv, int hd, const int32_t* block_table, int max_pages,
+                                  int page_size, int64_t n_pages, void* k_pool, void* v_pool, hipStream_t s) {
+  if (n_tokens == 0) return hipSuccess;
+  if (hd % 8 != 0) return hipErrorInvalidValue;
+  const int chunks = hd / 8;  // 16-byte pieces of a bf16 row
+  const int64_t threads = n_tokens * nkv * chunks;
+  hipLaunchKernelGGL(kv_append_paged_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), positions, n_tokens, seq_len, nkv,
+                     chunks, block_table, max_pages, page_size, n_pages, static_cast<u32x4*>(k_pool),
+                     static_cast<u32x4*>(v_pool));
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append_fp8(const void* k, const void* v, const int32_t* positions, int64_t n_tokens,
                                 int seq_len, int nkv, int hd, DType dt, void* k8, void* v8, float* k_scale,

@@ -20,7 +20,7 @@ states.  Pages cited (by title, section and equation; no line numbers):
 
 The 8-bit KV-cache model (``oracle.fp8``: E4M3 codes with one fp32 scale per
 cache row) is pinned against the format definition in
-``tests/test_oracle_fp8_pins.py``.
+``tests/test_oracle_kvcache_pins.py``.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_pins.py`` (closed forms, the [L3] worked example,
@@ -45,4 +45,5 @@ from .reference import (  # noqa: F401
 )
 from .bf16 import round_bf16  # noqa: F401
 from . import fp8  # noqa: F401
+from . import paged  # noqa: F401
 from . import bruteforce  # noqa: F401

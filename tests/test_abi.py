@@ -204,3 +204,25 @@ def test_fp8kv_validation():
                                      FAKE + 0x500, FAKE + 0x600, 64, 4, 256, 4, 2, 128, 512, 1e4, 1e-5, 0,
                                      FAKE + 0x700, need_b - 1, None)
     assert rc == -3
+
+
+def test_paged_validation():
+    L = binding.lib()
+
+    def att(**kw):
+        a = dict(q=FAKE, kp=FAKE + 0x100, vp=FAKE + 0x200, tab=FAKE + 0x300, maxp=16, P=64, npg=100,
+                 out=FAKE + 0x400, pos=FAKE + 0x500, B=2, nq=8, nkv=2, hd=128, ws=FAKE + 0x600, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.llama_gqa_attention_paged(a["q"], a["kp"], a["vp"], a["tab"], a["maxp"], a["P"], a["npg"], a["out"],
+                                           a["pos"], a["B"], a["nq"], a["nkv"], a["hd"], a["ws"], a["ws_bytes"], None)
+    assert att(P=48) == -2                 # page size not a multiple of 32
+    assert att(tab=None) == -1
+    assert att(npg=0) == -1
+    assert att(hd=64) == -2
+    assert att(pos=None) == -1
+    need = L.llama_gqa_attention_paged_workspace_bytes(2, 16, 64, 8, 2, 128)
+    assert need > 0
+    assert att(ws_bytes=need - 1) == -3
+    assert L.llama_kv_append_paged(FAKE, FAKE, FAKE, FAKE, 4, 48, 2, 1, 8, 128, FAKE, FAKE, 10, None) == -2
+    assert L.llama_kv_append_paged(FAKE, FAKE, FAKE, None, 4, 64, 2, 1, 8, 128, FAKE, FAKE, 10, None) == -1
+    assert L.llama_kv_append_paged(FAKE, FAKE, FAKE, FAKE, 4, 64, 2, 1, 8, 12, FAKE, FAKE, 10, None) == -2

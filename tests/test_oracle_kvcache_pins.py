@@ -1,7 +1,9 @@
-"""Pins of the oracle's 8-bit KV-cache model (oracle/fp8.py) against the
-E4M3 format definition and the scale convention it states ([LA]
-"Troubleshooting Common Deployment Faults", item 3, names the 8-bit cache;
-the format and scale are readings).  Nothing here uses a GPU."""
+"""Pins of the oracle's KV-cache variants against their definitions: the
+8-bit cache model (oracle/fp8.py) against the E4M3 format and the scale
+convention it states, and the paged-cache mapping (oracle/paged.py) against a
+scalar loop and its inverse ([LA] "Troubleshooting Common Deployment Faults",
+item 3, names both remedies; formats and layouts are readings).  Nothing here
+uses a GPU."""
 
 import numpy as np
 import pytest
@@ -145,3 +147,33 @@ def test_decode_step_fp8kv_reduces_to_plain_decode_for_zero_new_rows():
         assert np.all(ks2[b, :, p] == 0) and np.all(vs2[b, :, p] == 0)
         keep = [j for j in range(S) if j != p]
         assert np.array_equal(kc2[b][:, keep], kc[b][:, keep]) and np.array_equal(ks2[b][:, keep], ks[b][:, keep])
+
+
+# ---------------------------------------------------------------------------
+# paged cache mapping (oracle/paged.py)
+# ---------------------------------------------------------------------------
+def test_paged_gather_against_scalar_mapping():
+    from oracle import paged
+    g = rng(8)
+    P, n_pages, B, max_pages, nkv, hd = 4, 9, 2, 3, 2, 3
+    pool = g.standard_normal((n_pages, P, nkv, hd))
+    table = np.array([[5, 0, 7], [2, 8, 1]])
+    out = paged.gather(pool, table, P)
+    for b in range(B):
+        for j in range(max_pages * P):
+            assert np.array_equal(out[b, j], pool[table[b, j // P], j % P])
+
+
+def test_paged_identity_table_and_scatter_round_trip():
+    from oracle import paged
+    g = rng(9)
+    P, B, max_pages, nkv, hd = 8, 3, 4, 2, 16
+    cache = g.standard_normal((B, max_pages * P, nkv, hd))
+    ident = np.arange(B * max_pages).reshape(B, max_pages)
+    pool = cache.reshape(B * max_pages, P, nkv, hd)
+    assert np.array_equal(paged.gather(pool, ident, P), cache)
+    perm = g.permutation(20)[:B * max_pages].reshape(B, max_pages)
+    pool2 = paged.scatter(cache, perm, 20, P)
+    assert np.array_equal(paged.gather(pool2, perm, P), cache)
+    unused = sorted(set(range(20)) - set(perm.ravel()))
+    assert np.all(np.isnan(pool2[unused]))
