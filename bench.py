@@ -268,6 +268,40 @@ def bench_paged_attention(wd, dev, args, page_size=64):
             "frac": round(at_gbs / HBM_PEAK_GBS, 4)}
 
 
+def bench_lm_head(wd, dev, args, vocab=128256):
+    """The output layer after the decode step ([L3] §十): final RMSNorm, the
+    [4096 -> 128256] head and argmax for the 64 sequences' last positions.
+    The 1.05 GB head is drawn on the GPU by torch's seeded normal generator
+    (N(0, 0.02^2), rounded to bf16); the rows are the decode workload's x."""
+    inp = synth.make_block_inputs(wd)
+    d = wd.d_model
+    g = torch.Generator(device=dev).manual_seed(4000 + 20)
+    w = (torch.randn(vocab, d, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    gamma = inp.weights["ffn_norm"].to(dev)
+    h = inp.x.reshape(-1, d).to(dev)
+    need = binding.lib().llama_lm_head_argmax_workspace_bytes(h.shape[0], d, vocab, binding.BF16, binding.F32)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    ms, per, dk = time_steps(lambda: binding.lm_head_argmax(h, gamma, w, wd.eps, workspace=ws), args.decode_steps,
+                             args.warmup, flush=lambda: scratch.sum())
+    wbytes = vocab * d * 2
+    rows = {}
+    for key, (n, t) in sorted(dk.items(), key=lambda kv: -kv[1][1]):
+        rows[key] = {"launches": n, "avg_us": round(t / n * 1e3, 2)}
+    head_key = next((k for k in dk if k.startswith("lm_head")), None)
+    head_us = dk[head_key][1] / dk[head_key][0] * 1e3 if head_key else 0.0
+    gbs = wbytes / (head_us * 1e-6) / 1e9 if head_us else 0.0
+    log(f"[bench] output layer (final norm + head {d}->{vocab} + argmax, {h.shape[0]} rows): {ms * 1e3:.1f} us; "
+        f"head GEMM {head_us:.1f} us = {gbs:.0f} GB/s")
+    del w, ws, scratch
+    torch.cuda.empty_cache()
+    return {"workload": f"final RMSNorm + head [{vocab}, {d}] bf16 + argmax for {h.shape[0]} rows, last-level cache "
+                        f"flushed between calls",
+            "ms_per_call": round(ms, 4), "head_kernel": head_key, "head_avg_us": round(head_us, 2),
+            "head_bytes": wbytes, "head_gbs": round(gbs, 1), "head_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "kernels": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +409,7 @@ def main():
         torch.cuda.empty_cache()
         decode["fp8kv"] = bench_decode_fp8kv(wd, dev, args)
         decode["paged_attention"] = bench_paged_attention(wd, dev, args)
+        decode["lm_head"] = bench_lm_head(wd, dev, args)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -255,6 +255,26 @@ size_t llama_gqa_attention_paged_workspace_bytes(int32_t batch, int32_t max_page
                                                  int32_t n_q_heads, int32_t n_kv_heads,
                                                  int32_t head_dim);
 
+/* Output layer with the greedy choice ([L3] §十: after the last block a
+ * final RMSNorm, the linear head to vocabulary logits, and argmax, the
+ * deterministic one of the choices it lists; the head is applied to the last
+ * position of each sequence, so the caller passes those rows):
+ *   f = RMSNorm(h; gamma)   (as llama_rmsnorm: fp32 sum of squares, eps inside)
+ *   logits = f W_head^T     (fp32 accumulation and result)
+ *   token[r] = argmax_v logits[r, v]  (ties go to the smallest v; NaN is
+ *              never chosen)
+ * h: rdtype [n_rows, d_model]; gamma: wdtype [d_model]; w_head: wdtype
+ * [vocab, d_model] ([out, in]); token: int32 [n_rows]; logits (nullable):
+ * fp32 [n_rows, vocab] receives the logits (otherwise they stay in the
+ * workspace); best (nullable): fp32 [n_rows] receives each chosen logit.
+ * workspace: at least llama_lm_head_argmax_workspace_bytes(...) bytes. */
+int llama_lm_head_argmax(const void* h, const void* gamma, const void* w_head, int32_t* token,
+                         float* logits, float* best, int64_t n_rows, int32_t d_model, int32_t vocab,
+                         double eps, int wdtype, int rdtype, void* workspace, size_t ws_bytes,
+                         void* stream);
+size_t llama_lm_head_argmax_workspace_bytes(int64_t n_rows, int32_t d_model, int32_t vocab,
+                                            int wdtype, int rdtype);
+
 /* Host-only helpers. */
 const char* llama_last_error(void);    /* thread-local text of the last failure ("" if none) */
 const char* llama_status_string(int status);

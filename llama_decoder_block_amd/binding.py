@@ -25,7 +25,7 @@ FUNCTIONS = [
     "llama_profile_query", "llama_profile_names", "llama_kv_append_fp8", "llama_gqa_attention_fp8kv",
     "llama_gqa_attention_fp8kv_workspace_bytes", "llama_block_forward_fp8kv",
     "llama_block_forward_fp8kv_workspace_bytes", "llama_kv_append_paged", "llama_gqa_attention_paged",
-    "llama_gqa_attention_paged_workspace_bytes",
+    "llama_gqa_attention_paged_workspace_bytes", "llama_lm_head_argmax", "llama_lm_head_argmax_workspace_bytes",
 ]
 
 
@@ -91,6 +91,9 @@ def lib():
         "llama_gqa_attention_paged": ([_vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _vp,
                                        _sz, _vp], _int),
         "llama_gqa_attention_paged_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
+        "llama_lm_head_argmax": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _f64, _int, _int, _vp, _sz, _vp],
+                                 _int),
+        "llama_lm_head_argmax_workspace_bytes": ([_i64, _i32, _i32, _int, _int], _sz),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -295,6 +298,22 @@ def gqa_attention_paged(q, k_pages, v_pages, block_table, positions, out=None, w
     _check(L.llama_gqa_attention_paged(_p(q), _p(k_pages), _p(v_pages), _p(block_table), max_pages, P, n_pages,
                                        _p(out), _p(positions), B, nq, nkv, hd, _p(ws), nbytes, _stream()))
     return out
+
+
+# --- output layer ---------------------------------------------------------------
+def lm_head_argmax(h, gamma, w_head, eps, logits=None, best=None, workspace=None):
+    """Greedy tokens of rows h [N, d] (residual dtype): RMSNorm(h; gamma), head
+    w_head [vocab, d], argmax.  Returns int32 [N]; fills `logits` [N, vocab]
+    fp32 and `best` [N] fp32 when given."""
+    n, d = h.shape[0], h.shape[-1]
+    vocab = w_head.shape[0]
+    token = torch.empty(n, dtype=torch.int32, device=h.device)
+    L = lib()
+    need = L.llama_lm_head_argmax_workspace_bytes(n, d, vocab, _dt(w_head), _dt(h))
+    ws, nbytes = _workspace(need, h.device, workspace)
+    _check(L.llama_lm_head_argmax(_p(h), _p(gamma), _p(w_head), _p(token), _p(logits), _p(best), n, d, vocab, eps,
+                                  _dt(w_head), _dt(h), _p(ws), nbytes, _stream()))
+    return token
 
 
 # --- kernel timing -----------------------------------------------------------

@@ -748,6 +748,82 @@ int llama_gqa_attention_paged(const void* q, const void* k_pages, const void* v_
 }
 
 // ---------------------------------------------------------------------------
+// output layer: final RMSNorm, linear head, argmax
+// ---------------------------------------------------------------------------
+namespace {
+
+struct HeadPlan {
+  size_t f, logits, gemm, arg, total;
+};
+
+HeadPlan head_plan(int64_t n, int32_t d, int32_t vocab, DType wdt) {
+  HeadPlan p{};
+  p.f = align_up(static_cast<size_t>(n) * d * lb::dtype_bytes(wdt));
+  p.logits = align_up(static_cast<size_t>(n) * vocab * sizeof(float));
+  p.gemm = align_up(lb::gemm_workspace_bytes(wdt, static_cast<int>(n), vocab, d, false));
+  p.arg = align_up(lb::argmax_workspace_bytes(n, vocab));
+  p.total = p.f + p.logits + p.gemm + p.arg;
+  return p;
+}
+
+}  // namespace
+
+size_t llama_lm_head_argmax_workspace_bytes(int64_t n_rows, int32_t d_model, int32_t vocab, int wdtype,
+                                            int rdtype) {
+  if (n_rows <= 0 || n_rows > 0x7fffffff || d_model <= 0 || vocab <= 0 || !dtype_ok(wdtype) || !dtype_ok(rdtype))
+    return 0;
+  return head_plan(n_rows, d_model, vocab, static_cast<DType>(wdtype)).total;
+}
+
+int llama_lm_head_argmax(const void* h, const void* gamma, const void* w_head, int32_t* token, float* logits,
+                         float* best, int64_t n_rows, int32_t d_model, int32_t vocab, double eps, int wdtype,
+                         int rdtype, void* workspace, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(wdtype) || !dtype_ok(rdtype))
+    return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code (wdtype=%d rdtype=%d)", wdtype, rdtype);
+  if (n_rows < 0 || d_model <= 0 || vocab <= 0)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "n_rows must be >= 0; d_model, vocab > 0");
+  if (!(eps >= 0.0)) return fail(LLAMA_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  if (n_rows > 0x7fffffff) return fail(LLAMA_ERR_UNSUPPORTED, "n_rows too large");
+  if (n_rows == 0) return ok();
+  if (!h || !gamma || !w_head || !token)
+    return fail(LLAMA_ERR_INVALID_ARGUMENT, "h, gamma, w_head and token must be non-null");
+  for (const void* p : std::initializer_list<const void*>{h, gamma, w_head, static_cast<const void*>(token),
+                                                          static_cast<const void*>(logits),
+                                                          static_cast<const void*>(best), workspace})
+    if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  const DType wdt = static_cast<DType>(wdtype), rdt = static_cast<DType>(rdtype);
+  const HeadPlan p = head_plan(n_rows, d_model, vocab, wdt);
+  if (ws_bytes < p.total || !workspace)
+    return fail(LLAMA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", p.total, ws_bytes);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  void* f = ws;
+  float* lg = logits ? logits : reinterpret_cast<float*>(ws + p.f);
+  void* gws = ws + p.f + p.logits;
+  void* aws = ws + p.f + p.logits + p.gemm;
+  const int M = static_cast<int>(n_rows);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed("final_norm", s, [&](const char** name) {
+    *name = "rmsnorm";
+    return lb::launch_rmsnorm(h, nullptr, gamma, f, nullptr, M, d_model, static_cast<float>(eps), wdt, rdt, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_lm_head_argmax: final norm");
+  lb::WSeg wh{};
+  wh.ptr[0] = w_head; wh.start[0] = 0; wh.start[1] = vocab; wh.nseg = 1;
+  lb::GemmEpi ep{};
+  ep.kind = lb::EpiKind::Store; ep.out_dt = DType::F32; ep.out = lg; ep.ldo = vocab;
+  e = timed("lm_head", s, [&](const char** name) {
+    return lb::launch_gemm(wdt, f, M, d_model, wh, vocab, false, ep, gws, p.gemm, s, name);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_lm_head_argmax: head projection");
+  e = timed("argmax", s, [&](const char** name) {
+    *name = "argmax";
+    return lb::launch_argmax_rows(lg, M, vocab, vocab, token, best, aws, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "llama_lm_head_argmax: argmax");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
 int llama_profile_enable(int on) {
   g_prof_on = on != 0;
   return ok();

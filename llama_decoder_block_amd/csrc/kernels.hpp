@@ -337,6 +337,12 @@ hipError_t launch_kv_append_paged(const void* k, const void* v, const int32_t* p
                                   int seq_len, int nkv, int hd, const int32_t* block_table, int max_pages,
                                   int page_size, int64_t n_pages, void* k_pool, void* v_pool, hipStream_t s);
 
+// token[r] = argmax over the n fp32 logits of row r (row stride ld; ties go to
+// the smallest column); best_value (nullable) receives the maximum.
+size_t argmax_workspace_bytes(int64_t rows, int n);
+hipError_t launch_argmax_rows(const float* logits, int64_t rows, int64_t ld, int n, int32_t* token,
+                              float* best_value, void* ws, hipStream_t s);
+
 // Quantizes rows k, v [n_tokens, nkv, hd] (dtype dt) and stores them at slot
 // positions[n] of sequence n / seq_len (tokens whose slot is outside
 // [0, kv_cap) are skipped).  hd must be a multiple of 64, at most 256.

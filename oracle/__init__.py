@@ -46,4 +46,5 @@ from .reference import (  # noqa: F401
 from .bf16 import round_bf16  # noqa: F401
 from . import fp8  # noqa: F401
 from . import paged  # noqa: F401
+from . import head  # noqa: F401
 from . import bruteforce  # noqa: F401

@@ -226,3 +226,17 @@ def test_paged_validation():
     assert L.llama_kv_append_paged(FAKE, FAKE, FAKE, FAKE, 4, 48, 2, 1, 8, 128, FAKE, FAKE, 10, None) == -2
     assert L.llama_kv_append_paged(FAKE, FAKE, FAKE, None, 4, 64, 2, 1, 8, 128, FAKE, FAKE, 10, None) == -1
     assert L.llama_kv_append_paged(FAKE, FAKE, FAKE, FAKE, 4, 64, 2, 1, 8, 12, FAKE, FAKE, 10, None) == -2
+
+
+def test_lm_head_validation():
+    L = binding.lib()
+    need = L.llama_lm_head_argmax_workspace_bytes(64, 4096, 128256, 1, 0)
+    assert need >= 64 * 128256 * 4
+    assert L.llama_lm_head_argmax(FAKE, FAKE, FAKE, None, None, None, 64, 4096, 128256, 1e-5, 1, 0, FAKE, need,
+                                  None) == -1                     # no token output
+    assert L.llama_lm_head_argmax(FAKE, FAKE, FAKE, FAKE, None, None, 64, 4096, 0, 1e-5, 1, 0, FAKE, need,
+                                  None) == -1                     # vocab 0
+    assert L.llama_lm_head_argmax(FAKE, FAKE, FAKE, FAKE, None, None, 64, 4096, 128256, 1e-5, 1, 0, FAKE, need - 1,
+                                  None) == -3
+    assert L.llama_lm_head_argmax(FAKE, FAKE, FAKE, FAKE + 4, None, None, 64, 4096, 128256, 1e-5, 1, 0, FAKE, need,
+                                  None) == -2                     # misaligned

@@ -443,3 +443,44 @@ def test_round_bf16_against_torch_cast():
     np.testing.assert_array_equal(ours, ref)
     assert oracle.round_bf16(1.0 + 2.0 ** -8) == 1.0            # tie to even (down)
     assert oracle.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6  # tie to even (up)
+
+
+# ---------------------------------------------------------------------------
+# output layer ([L3] §十): final RMSNorm, head, greedy choice
+# ---------------------------------------------------------------------------
+def test_greedy_token_against_scalar_loop_with_ties_and_nan():
+    from oracle import head
+    g = rng(60)
+    lg = np.round(g.standard_normal((20, 50)) * 4) / 4       # many exact ties
+    lg[3, :] = 1.0
+    lg[4, 7] = np.nan
+    lg[4, 9] = 100.0
+    got = head.greedy_token(lg)
+    for r in range(lg.shape[0]):
+        best, bi = -np.inf, 0
+        for c in range(lg.shape[1]):
+            v = lg[r, c]
+            if not np.isnan(v) and v > best:
+                best, bi = v, c
+        assert got[r] == bi
+    assert got[3] == 0 and got[4] == 9
+
+
+def test_lm_head_planted_maximum():
+    # a head row aligned with the normalized row: its logit is exactly alpha,
+    # far above the others, so it is chosen; the logits are RMSNorm then the
+    # [out, in] product
+    from oracle import head
+    g = rng(61)
+    d, vocab = 64, 300
+    h = g.standard_normal((3, d))
+    gamma = 1.0 + 0.1 * g.standard_normal(d)
+    w = 0.01 * g.standard_normal((vocab, d))
+    f = oracle.rmsnorm(h, gamma, 1e-5)
+    for r, v in enumerate((17, 250, 3)):
+        w[v] = 30.0 * f[r] / np.dot(f[r], f[r])
+    lg = head.lm_head_logits(h, gamma, w, 1e-5)
+    assert lg.shape == (3, vocab)
+    assert np.allclose([lg[0, 17], lg[1, 250], lg[2, 3]], 30.0)
+    assert list(head.greedy_token(lg)) == [17, 250, 3]
+    np.testing.assert_allclose(lg, f @ w.T)
