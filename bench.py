@@ -29,6 +29,8 @@ cpu_baseline = the CPU oracle (numpy fp64) on a bounded sample of the same
 import argparse
 import json
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -150,9 +152,11 @@ def cpu_baseline(tokens):
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max((i.get("num_threads", 1) for i in pools), default=1)
+        blas = ",".join(sorted({str(i.get("internal_api")) for i in pools})) or "unknown"
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        threads, blas = len(os.sched_getaffinity(0)), "unknown"
     wl = synth.workload(PREFILL, seq=tokens)
     inp = synth.make_block_inputs(wl)
     f = inp.as_f64()
@@ -162,7 +166,78 @@ def cpu_baseline(tokens):
     flops = wm.prefill_flops(shape_of(wl), wl.batch, wl.seq)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"numpy fp64 block forward of the first {tokens} of the {synth.workload(PREFILL).seq} "
-                      f"tokens of the Llama-3-8B prefill (same seeded inputs), one pass, {dt:.1f} s"}
+                      f"tokens of the Llama-3-8B prefill (same seeded inputs), one pass, {dt:.1f} s, BLAS {blas}"}
+
+
+def device_info():
+    """Agent name, compute units and peak clock from rocminfo (run before this
+    process touches the GPU; a child process, never an exec)."""
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except Exception as e:  # pragma: no cover
+        return {"error": f"rocminfo: {e}"}
+    for blk in out.split("Agent ")[1:]:
+        if not re.search(r"Device Type:\s+GPU", blk):
+            continue
+        def field(name):
+            m = re.search(name + r":[ \t]*([^\n]*)", blk)
+            return m.group(1).strip() if m and m.group(1).strip() else None
+        cu, clk = field("Compute Unit"), field(r"Max Clock Freq\. \(MHz\)")
+        return {"name": field("Name"),
+                "compute_units": int(cu) if cu and cu.isdigit() else cu,
+                "max_clock_mhz": int(clk) if clk and clk.isdigit() else clk}
+    return {"error": "no GPU agent in rocminfo"}
+
+
+def copy_bandwidth(dev, reps=10):
+    """A plain 1 GiB device copy (1 GiB read + 1 GiB written), timed with
+    events: the measured HBM rate, reported beside the 8 TB/s specification."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * src.numel() * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"[bench] device copy 1 GiB: {ms * 1e3:.1f} us = {gbs:.0f} GB/s")
+    return {"bytes_per_copy": 2 * (1 << 30), "us": round(ms * 1e3, 1), "gbs": round(gbs, 1),
+            "frac_of_spec": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def bench_rope(wl, dev, args):
+    """The standalone RoPE entry point on the prefill's Q and K
+    ([T, n_q, hd] and [T, n_kv, hd] bf16, positions 0..T-1), rotated in
+    place: HBM-bound, each element read and written once."""
+    T, nq, nkv, hd = wl.batch * wl.seq, wl.n_q, wl.n_kv, wl.head_dim
+    q = synth.normal(1000 * wl.index + 90, (T, nq, hd), dtype="bf16").to(dev)
+    k = synth.normal(1000 * wl.index + 91, (T, nkv, hd), dtype="bf16").to(dev)
+    pos = torch.arange(T, dtype=torch.int32, device=dev)
+    # Q and K (84 MB) would fit in the 256 MB last-level cache: a 1 GiB read
+    # between calls makes every call stream from HBM
+    scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    ms, _, kernels = time_steps(lambda: binding.rope(q, k, pos, wl.theta), 20, args.warmup,
+                                flush=lambda: scratch.sum())
+    nbytes = 2 * (q.numel() + k.numel()) * q.element_size()
+    n, t = kernels.get("rope", (0, 0.0))
+    avg_us = t / n * 1e3 if n else ms * 1e3  # the library's own events around the launch
+    gbs = nbytes / (avg_us * 1e-6) / 1e9
+    log(f"[bench] standalone RoPE on Q [{T},{nq},{hd}] + K [{T},{nkv},{hd}] bf16: {ms * 1e3:.1f} us per call "
+        f"= {gbs:.0f} GB/s (event-timed inside the library: {avg_us:.1f} us)")
+    del q, k, pos, scratch
+    torch.cuda.empty_cache()
+    return {"workload": f"RoPE in place on Q [{T},{nq},{hd}] and K [{T},{nkv},{hd}] bf16, positions 0..{T - 1}, "
+                        f"theta {wl.theta:g}, last-level cache flushed between calls",
+            "us_per_call": round(ms * 1e3, 2), "bytes": nbytes, "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "kernel_avg_us": round(avg_us, 2)}
 
 
 def bench_decode_fp8kv(wd, dev, args):
@@ -318,6 +393,7 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: there is no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    device = None if args.copy_calibration else device_info()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -331,6 +407,9 @@ def main():
         log(f"[bench] copy calibration: 5 x {src.numel() * 4} bytes read and written")
         return
     binding.lib()
+    if device is not None:
+        log(f"[bench] device: {device}")
+    copy_bw = copy_bandwidth(dev)
 
     # ---------------- prefill -----------------
     wl = synth.workload(PREFILL)
@@ -354,6 +433,7 @@ def main():
         log(f"[bench]   {k:40s} {row}")
     del step
     torch.cuda.empty_cache()
+    rope = bench_rope(wl, dev, args)
 
     # ---------------- decode -----------------
     decode = None
@@ -442,7 +522,10 @@ def main():
                      "frac": round(dom_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": dominant_traffic(),
                      "flops_per_launch": dom_flops, "avg_us": round(dom_avg_ms * 1e3, 2)},
         "kernels": table,
+        "rope": rope,
         "decode": decode,
+        "device": device,
+        "hbm_copy": copy_bw,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

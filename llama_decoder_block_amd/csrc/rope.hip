@@ -3,9 +3,15 @@
 // Adjacent pairs (x_2k, x_2k+1) of each head at position m are rotated by
 // m * theta^(-2k/hd) ("Llama Architecture: RMSNorm, SwiGLU, RoPE, GQA, and
 // PyTorch Implementation" §3, rotation matrix; "LLaMA-3 8B 现代 LLM 架构、计算规模与能耗"
-// §四.3).  Each thread handles four consecutive elements (two pairs) of one
-// token row, so a wavefront reads and writes 64 x 4 contiguous elements.
-// HBM-bound: every element of Q and K is read once and written once.
+// §四.3).  HBM-bound: every element of Q and K is read once and written once.
+//
+// Main kernel (head_dim a multiple of one 16-byte vector): one launch covers Q
+// and K.  A thread owns one 16-byte column vector of the head (8 bf16 or 4
+// fp32 elements) at one token, forms that vector's angles once, and applies
+// them to the same column of up to kHeadsPerThread heads (Q heads first, then
+// K heads), whose loads are all issued before the first store.  Sixteen
+// lanes cover one 256-byte head row of bf16, so every access is a whole
+// 16-byte vector in a contiguous run.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,6 +43,82 @@ rope_kernel(T* __restrict__ x, const int32_t* __restrict__ positions, int64_t n_
     v[2 * pr + 1] = a * s + b * c;
   }
   Vec4<T>::store(p, v);
+}
+
+constexpr int kHeadsPerThread = 8;
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+rope_heads_kernel(T* __restrict__ q, T* __restrict__ k, const int32_t* __restrict__ positions,
+                  int64_t n_tokens, int nq, int nkv, int hd, int chunks, RopeTable rope) {
+  constexpr int E = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte vector
+  constexpr int P = E / 2;                              // pairs per vector
+  const int vecs = hd / E;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= n_tokens * chunks * vecs) return;
+  const int vi = static_cast<int>(gid % vecs);
+  const int64_t rest = gid / vecs;
+  const int chunk = static_cast<int>(rest % chunks);
+  const int64_t tok = rest / chunks;
+  const int pos = positions[tok];
+  float sn[P], cs[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) rope_sincos_t<T>(pos, rope.inv_freq[vi * P + p], &sn[p], &cs[p]);
+
+  const int h0 = chunk * kHeadsPerThread;
+  const int nh = min(kHeadsPerThread, nq + nkv - h0);
+  u32x4* ptr[kHeadsPerThread];
+  u32x4 v[kHeadsPerThread];
+#pragma unroll
+  for (int j = 0; j < kHeadsPerThread; ++j) {
+    const int h = h0 + j;
+    T* row = h < nq ? q + (tok * nq + h) * static_cast<int64_t>(hd)
+                    : k + (tok * nkv + (h - nq)) * static_cast<int64_t>(hd);
+    ptr[j] = reinterpret_cast<u32x4*>(row + vi * E);
+    if (j < nh) v[j] = *ptr[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kHeadsPerThread; ++j) {
+    if (j >= nh) break;
+    float x[E];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        x[2 * w] = __uint_as_float(v[j][w] << 16);
+        x[2 * w + 1] = __uint_as_float(v[j][w] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x[w] = __uint_as_float(v[j][w]);
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const float a = x[2 * p], b = x[2 * p + 1];
+      x[2 * p] = a * cs[p] - b * sn[p];
+      x[2 * p + 1] = a * sn[p] + b * cs[p];
+    }
+    u32x4 o;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(x[2 * w], x[2 * w + 1]);
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[w] = __float_as_uint(x[w]);
+    }
+    *ptr[j] = o;
+  }
+}
+
+template <typename T>
+hipError_t rope_heads(T* q, T* k, const int32_t* positions, int64_t n_tokens, int nq, int nkv, int hd,
+                      const RopeTable& rope, hipStream_t s) {
+  constexpr int E = 16 / static_cast<int>(sizeof(T));
+  const int chunks = (nq + nkv + kHeadsPerThread - 1) / kHeadsPerThread;
+  const int64_t n = n_tokens * chunks * (hd / E);
+  const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+  hipLaunchKernelGGL((rope_heads_kernel<T>), dim3(blocks), dim3(256), 0, s, q, k, positions, n_tokens, nq, nkv,
+                     hd, chunks, rope);
+  return hipGetLastError();
 }
 
 // Fallback for rows whose length is not a multiple of 4: one thread per pair.
@@ -109,6 +191,13 @@ hipError_t launch_rope_table(const int32_t* positions, int64_t n_tokens, int hd,
 hipError_t launch_rope(void* q, void* k, const int32_t* positions, int64_t n_tokens, int nq,
                        int nkv, int hd, const RopeTable& rope, DType dt, hipStream_t s) {
   if (n_tokens == 0) return hipSuccess;
+  const int nq_used = q ? nq : 0, nkv_used = k ? nkv : 0;
+  if (hd % (dt == DType::F32 ? 4 : 8) == 0)
+    return dt == DType::F32
+               ? rope_heads(static_cast<float*>(q), static_cast<float*>(k), positions, n_tokens, nq_used,
+                            nkv_used, hd, rope, s)
+               : rope_heads(static_cast<bf16_t*>(q), static_cast<bf16_t*>(k), positions, n_tokens, nq_used,
+                            nkv_used, hd, rope, s);
   hipError_t e = hipSuccess;
   if (q) {
     e = dt == DType::F32

@@ -69,19 +69,24 @@ def test_rmsnorm_constant_rows():
 # RoPE
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("hd,theta", [(128, 5e5), (128, 1e4), (64, 1e4), (2, 1e4)])
-def test_rope(dtype, hd, theta):
+@pytest.mark.parametrize("hd,theta", [(128, 5e5), (128, 1e4), (64, 1e4), (256, 1e4), (12, 1e4), (2, 1e4)])
+@pytest.mark.parametrize("nq,nkv", [(8, 2), (32, 8), (5, 0), (0, 3)])
+def test_rope(dtype, hd, theta, nq, nkv):
+    """Ragged head counts (a last group of fewer than 8 heads), Q only, K only;
+    head_dim 12 and 2 take the per-pair kernels for bf16."""
     n = 333
-    q = synth.normal(31, (n, 8, hd), dtype=dtype)
-    k = synth.normal(32, (n, 2, hd), dtype=dtype)
+    q = synth.normal(31, (n, nq, hd), dtype=dtype) if nq else None
+    k = synth.normal(32, (n, nkv, hd), dtype=dtype) if nkv else None
     pos = torch.from_numpy(np.random.Generator(np.random.PCG64(33)).integers(0, 8192, n).astype(np.int32))
     pos[:3] = torch.tensor([0, 1, 8191], dtype=torch.int32)
-    qd, kd = dev(q), dev(k)
+    qd = dev(q) if q is not None else None
+    kd = dev(k) if k is not None else None
     binding.rope(qd, kd, dev(pos), theta)
     torch.cuda.synchronize()
-    ref_q = oracle.rope(to64(q), to64(pos), theta)
-    ref_k = oracle.rope(to64(k), to64(pos), theta)
-    for got, ref, name in ((qd, ref_q, "q"), (kd, ref_k, "k")):
+    for src, got, name in ((q, qd, "q"), (k, kd, "k")):
+        if src is None:
+            continue
+        ref = oracle.rope(to64(src), to64(pos), theta)
         g = to64(got)
         pn = np.sqrt(ref[..., 0::2] ** 2 + ref[..., 1::2] ** 2)
         pair_norm = np.repeat(pn, 2, axis=-1)
@@ -90,8 +95,8 @@ def test_rope(dtype, hd, theta):
         else:
             bound = BF16_ULP * np.abs(ref) + 2e-6 * pair_norm + 1e-7
         assert np.all(np.abs(g - ref) <= bound), (name, np.max(np.abs(g - ref) - bound))
-    # position 0 leaves the vector unchanged
-    np.testing.assert_array_equal(to64(qd[0]), to64(q[0]))
+        # position 0 leaves the vector unchanged
+        np.testing.assert_array_equal(to64(got[0]), to64(src[0]))
 
 
 # ---------------------------------------------------------------------------
