@@ -305,9 +305,12 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
     // Lazy rescaling: the reference maximum m_run only moves when a row's
     // tile maximum exceeds it by more than kRescale (log2 units), so most
     // tiles skip rescaling O and l.  Any reference gives the same softmax;
-    // the weights stay <= 2^kRescale.
+    // the weights stay <= 2^kRescale.  The reference is kept an integer, so
+    // rescaling multiplies by an exact power of two and each weight's bf16
+    // rounding is that of exp2(score * c - M) for any integer M: the same
+    // whatever the tile order.
     if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescale) != 0) {
-      const float m_new = fmaxf(m_run, tmax);
+      const float m_new = ceilf(fmaxf(m_run, tmax));
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;

@@ -14,7 +14,10 @@ Conventions (readings of the pages, each stated where it is used):
 All arithmetic is float64.  With ``bf16_storage=True`` the value of every
 tensor the bf16 path stores in bf16 (a, q and k after RoPE, v, o, f, the
 SwiGLU product) is rounded RNE to bf16 before it is used; accumulations, the
-softmax weights and the residual stream h, y are never rounded.
+softmax denominator and the residual stream h, y are never rounded.  On the
+prefill path (more than one query token per sequence) the bf16 path also
+feeds the unnormalised softmax weights to its weighted sum of V in bf16: that
+rounding is modelled by :func:`bf16_prefill_weights`.
 """
 
 import numpy as np
@@ -102,9 +105,25 @@ def softmax_last(s):
 # position are masked; softmax over keys; output is the weighted sum of V
 # ([L3] §4.5); heads are concatenated in order h = 0..n_q-1 ([L3] §4.7).
 # ----------------------------------------------------------------------------
-def gqa_attention(q, k, v, visible_upto):
+def bf16_prefill_weights(s):
+    """Storage-point model of the prefill path's softmax weights, for scaled
+    scores ``s`` [..., S] (-inf where masked): with z = s * log2(e) and the
+    integer offset M = ceil(max z) per row, the weights exp2(z - M) enter the
+    weighted sum of V rounded RNE to bf16, while the denominator sums them
+    unrounded.  Multiplying a weight by a power of two commutes with the
+    rounding, so any integer offset gives the same normalised result.
+    Returns (rounded weights, denominator [..., 1])."""
+    z = _as64(s) * np.log2(np.e)
+    m = np.ceil(np.max(z, axis=-1, keepdims=True))
+    e = np.exp2(z - m)
+    return round_bf16(e), np.sum(e, axis=-1, keepdims=True)
+
+
+def gqa_attention(q, k, v, visible_upto, bf16_weights=False):
     """q [B, Tq, n_q, hd]; k, v [B, S, n_kv, hd]; visible_upto [B, Tq] int:
     query (b, t) sees key slots 0..visible_upto[b, t].  Returns [B, Tq, n_q, hd].
+    ``bf16_weights`` applies :func:`bf16_prefill_weights` (storage-point
+    model of the prefill path) in place of the exact softmax.
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, Tq, n_q, hd = q.shape
@@ -120,8 +139,11 @@ def gqa_attention(q, k, v, visible_upto):
             g = h // r
             s = (q[b, :, h, :] @ k[b, :, g, :].T) * scale  # [Tq, S]
             s = np.where(mask, -np.inf, s)
-            p = softmax_last(s)
-            out[b, :, h, :] = p @ v[b, :, g, :]
+            if bf16_weights:
+                wr, den = bf16_prefill_weights(s)
+                out[b, :, h, :] = (wr @ v[b, :, g, :]) / den
+            else:
+                out[b, :, h, :] = softmax_last(s) @ v[b, :, g, :]
     return out
 
 
@@ -189,7 +211,7 @@ def block_forward(x, w, positions, theta, eps, n_q, n_kv,
             kk[b, pos[b]] = k[b]
             vv[b, pos[b]] = v[b]
         vis = pos
-    o = gqa_attention(q, kk, vv, vis).reshape(B, T, -1)
+    o = gqa_attention(q, kk, vv, vis, bf16_weights=bf16_storage and T > 1).reshape(B, T, -1)
     h, y = _block_tail(x, o, w, eps, bf16_storage)
     if not return_intermediates:
         return y
@@ -231,7 +253,7 @@ def block_forward_rows(x, w, positions, rows, theta, eps, n_q, n_kv,
         ti = np.asarray(ts)
         q = linear(a[:, ti], w["wq"]).reshape(1, len(ts), n_q, hd)
         q = _store(rope(q, pos[b:b + 1, ti], theta), bf16_storage)
-        o = gqa_attention(q, k, v, ti[None, :]).reshape(1, len(ts), -1)
+        o = gqa_attention(q, k, v, ti[None, :], bf16_weights=bf16_storage and T > 1).reshape(1, len(ts), -1)
         h, y = _block_tail(xb[:, ti], o, w, eps, bf16_storage)
         order = {t: i for i, t in enumerate(ts)}
         for t in ts:

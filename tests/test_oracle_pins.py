@@ -445,6 +445,104 @@ def test_round_bf16_against_torch_cast():
     assert oracle.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6  # tie to even (up)
 
 
+# --------------------------------------------------------------------------
+# storage-point model of the prefill path's softmax weights (bf16 weights,
+# integer log2 offset, unrounded denominator)
+# --------------------------------------------------------------------------
+def attend_one(scores, v, bf16_weights):
+    """One query over len(scores) keys (V rows of width <= 4) through
+    oracle.gqa_attention with hd = 4: q = e_0 and k_j = 2 s_j e_0, so that
+    q.k_j / sqrt(4) is exactly s_j."""
+    S = len(scores)
+    v = np.asarray(v, dtype=np.float64).reshape(S, -1)
+    q = np.zeros((1, 1, 1, 4))
+    q[..., 0] = 1.0
+    k = np.zeros((1, S, 1, 4))
+    k[0, :, 0, 0] = 2.0 * np.asarray(scores, dtype=np.float64)
+    vv = np.zeros((1, S, 1, 4))
+    vv[0, :, 0, :v.shape[1]] = v
+    out = oracle.gqa_attention(q, k, vv, np.array([[S - 1]]), bf16_weights=bf16_weights)
+    return out[0, 0, 0, :v.shape[1]]
+
+
+def test_prefill_weights_hand_example():
+    """Scores 0.3 and -0.2 in log2 units: offset ceil(0.3) = 1, weights 2^-0.7
+    and 2^-1.2 round to the bf16 values 0.6171875 (158/256) and 0.435546875
+    (223/512); the denominator keeps the unrounded sum."""
+    ln2 = math.log(2.0)
+    out = attend_one([0.3 * ln2, -0.2 * ln2], [[1.0, 0.0], [0.0, 1.0]], True)
+    den = 2.0 ** -0.7 + 2.0 ** -1.2
+    np.testing.assert_allclose(out, [0.6171875 / den, 0.435546875 / den], rtol=1e-14)
+    # an offset without the ceiling (0.3) would give weights 1 and bf16(2^-0.5)
+    assert abs(out[0] - 1.0 / (1.0 + 2.0 ** -0.5)) > 1e-3
+
+
+def test_prefill_weights_uniform_scores_give_mean():
+    """Equal scores c: every weight is e = 2^(z - ceil z), z = c log2(e),
+    rounded to the same bf16 value, over a denominator of 7e, so the output
+    is mean(v) scaled by bf16(e) / e (exactly the mean when z is an integer)."""
+    g = rng(28)
+    v = g.standard_normal((7, 4))
+    for c in (0.0, 2.5, -13.0):
+        z = c * math.log2(math.e)
+        e = 2.0 ** (z - math.ceil(z))
+        r = oracle.round_bf16(e) / e
+        np.testing.assert_allclose(attend_one([c] * 7, v, True), v.mean(axis=0) * r, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(attend_one([0.0] * 7, v, True), v.mean(axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_prefill_weights_representable_equal_exact():
+    """Scores whose weights are powers of two (bf16-exact) give the exact
+    softmax result."""
+    g = rng(29)
+    z = np.array([0.0, -1.0, -2.0, -5.0, -3.0, 1.0, -7.0])
+    v = g.standard_normal((7, 4))
+    got = attend_one(z * math.log(2.0), v, True)
+    w = 2.0 ** z
+    np.testing.assert_allclose(got, (w / w.sum()) @ v, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(got, attend_one(z * math.log(2.0), v, False), rtol=1e-13, atol=1e-15)
+
+
+def test_prefill_weights_within_bf16_bound():
+    """Each weight carries a relative error of at most 2^-8, so the output
+    stays within 2^-8 * sum_j p_j |v_j| of the exact softmax result."""
+    g = rng(30)
+    for _ in range(50):
+        S = int(g.integers(1, 200))
+        s = g.standard_normal(S) * 4
+        v = g.standard_normal((S, 3))
+        got = attend_one(s, v, True)
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        exact = p @ v
+        assert np.all(np.abs(got - exact) <= 2.0 ** -8 * (p @ np.abs(v)) + 1e-15)
+
+
+def test_block_storage_weights_only_on_prefill_path():
+    """The bf16 weight model applies to calls with more than one query token;
+    a one-token call (the decode path) keeps the exact softmax."""
+    g = rng(31)
+    d, nq, nkv, hd, dff = 32, 4, 2, 8, 48
+    w = rand_weights(g, d, nq, nkv, hd, dff, scale=0.3)
+    x = g.standard_normal((1, 6, d))
+    pos = np.arange(6)[None, :]
+    y_st, inter = oracle.block_forward(x, w, pos, 1e4, 1e-5, nq, nkv, bf16_storage=True,
+                                       return_intermediates=True)
+    vis = np.broadcast_to(np.arange(6)[None, :], (1, 6))
+    o_model = oracle.gqa_attention(inter["q"], inter["k"], inter["v"], vis, bf16_weights=True)
+    o_exact = oracle.gqa_attention(inter["q"], inter["k"], inter["v"], vis)
+    np.testing.assert_allclose(inter["o"], o_model.reshape(1, 6, -1), rtol=0, atol=0)
+    assert np.abs(o_model - o_exact).max() > 0
+    # one token against a cache: exact weights
+    kc = np.zeros((1, 8, nkv, hd))
+    vc = np.zeros((1, 8, nkv, hd))
+    kc[:, :6], vc[:, :6] = inter["k"], inter["v"]
+    _, i1 = oracle.block_forward(x[:, 5:6], w, pos[:, 5:6], 1e4, 1e-5, nq, nkv, kc, vc, bf16_storage=True,
+                                 return_intermediates=True)
+    o1 = oracle.gqa_attention(i1["q"], i1["k_cache"], i1["v_cache"], np.array([[5]]))
+    np.testing.assert_allclose(i1["o"], o1.reshape(1, 1, -1), rtol=0, atol=0)
+
+
 # ---------------------------------------------------------------------------
 # output layer ([L3] §十): final RMSNorm, head, greedy choice
 # ---------------------------------------------------------------------------
