@@ -452,42 +452,70 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
   // epilogue: register e of a 32x32 tile is feature row (e/4)*8 + half*4 + e%4
   // of the weight operand and token column lane%32
   if constexpr (!DUAL) {
-    // Whole tile inside the output: the split epilogue.  Each lane's four
-    // token rows are resolved first, then the loads (or factors) of the next
-    // token row's 16 column groups are issued before the current row's
-    // results are stored, so every load overlaps other loads and stores.
+    // Whole tile inside the output: the staged epilogue.  The K loop's LDS
+    // buffers are free now; each wavefront passes its 128 x 128 block through
+    // its own LDS region one 32-token block at a time, so that afterwards a
+    // lane holds four consecutive columns of one token and each store (and
+    // each load of pre(), e.g. the residual or the rotation table) covers
+    // whole rows: 32 lanes x 16 bytes of one token, instead of 32 tokens x
+    // 16 bytes.  The next block's pre() loads are issued before the current
+    // block is stored.  Per-token keys (positions) are loaded once for all
+    // four blocks and shared between lanes.
     if (m0 + BM <= M && out_n0 + BN <= N && epi.vec_ok()) {
-      typename Epi::Row rows[TM];
+      constexpr int SROW = WN + 4;  // floats per staged token row (16 lanes of a read hit 64 distinct banks)
+      __syncthreads();              // every wavefront is done with the K loop's fragments
+      // lane values derived from a copy made here, so that nothing of the
+      // epilogue is computed before the K loop and kept live through it
+      int le = lane;
+      asm volatile("" : "+v"(le));
+      float* stage = reinterpret_cast<float*>(&lds[0][0]) + wid * (32 * SROW);
+      const int g = le & 31, hsel = le >> 5, srow = le & 31, shalf = le >> 5;
+      const int n = out_n0 + wave_n * WN + g * 4;
+      const int mw = m0 + wave_m * WM;
+      int key[TM];
 #pragma unroll
-      for (int b = 0; b < TM; ++b) rows[b] = epi.row(m0 + wave_m * WM + b * 32 + frag_row);
-      f32x4 pre[2][TN * 4];
-      auto col = [&](int a, int j) { return out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4; };
-      auto issue = [&](int b) {
-#pragma unroll
-        for (int a = 0; a < TN; ++a)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pre[b & 1][a * 4 + j] = epi.pre(rows[b], col(a, j));
+      for (int b = 0; b < TM; ++b) key[b] = Epi::kRowKey ? epi.row_key(mw + b * 32 + g) : 0;
+      // row of token 2i + hsel of block b (iteration i: lanes 0-31 one token, 32-63 the next)
+      auto row_of = [&](int b, int i) {
+        const int t = 2 * i + hsel;
+        return epi.row_from(mw + b * 32 + t, Epi::kRowKey ? __shfl(key[b], t, 64) : 0);
       };
-      auto finish = [&](int b) {
+      // chunks of CH iterations (16 / CH per block); chunk c + 1's pre()
+      // loads are issued before chunk c is stored.  CH is the largest that
+      // leaves the K loop free of register spills for each epilogue.
+      constexpr int CH = Epi::kRowKey ? 8 : 4, NCH = 16 / CH;
+      f32x4 pre[2][CH];
+      auto issue = [&](int c) {
 #pragma unroll
-        for (int a = 0; a < TN; ++a)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
-            epi.put(rows[b], col(a, j), pre[b & 1][a * 4 + j], v);
-          }
+        for (int i = 0; i < CH; ++i) pre[c & 1][i] = epi.pre(row_of(c / NCH, (c % NCH) * CH + i), n);
       };
-      // (scheduling fences keep the accumulators in AGPRs until their row's
-      // turn, leaving VGPRs for the in-flight loads)
       issue(0);
 #pragma unroll
-      for (int b = 0; b < TM; ++b) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (b + 1 < TM) issue(b + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        finish(b);
+      for (int c = 0; c < NCH * TM; ++c) {
+        const int b = c / NCH, i0 = (c % NCH) * CH;
+        if (i0 == 0) {
+          // register e of tile (a, b): token frag_row, column a*32 + (e/4)*8 + frag_half*4 + e%4
+#pragma unroll
+          for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              f32x4 t = f32x4{acc[a][b][4 * j], acc[a][b][4 * j + 1], acc[a][b][4 * j + 2], acc[a][b][4 * j + 3]};
+              asm volatile("" : "+v"(t));  // through VGPRs (left to itself the allocator spills in the K loop)
+              *reinterpret_cast<f32x4*>(stage + srow * SROW + a * 32 + j * 8 + shalf * 4) = t;
+            }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        f32x4 val[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+          val[i] = *reinterpret_cast<const f32x4*>(stage + (2 * (i0 + i) + hsel) * SROW + g * 4);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next block overwrites it
+        if (c + 1 < NCH * TM) issue(c + 1);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const float v[4] = {val[i][0], val[i][1], val[i][2], val[i][3]};
+          epi.put(row_of(b, i0 + i), n, pre[c & 1][i], v);
+        }
       }
       return;
     }

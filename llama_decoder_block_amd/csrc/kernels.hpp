@@ -37,7 +37,10 @@ struct WSeg {
 // pre(row, n) issues the group's loads (or computes its factors), and
 // put(row, n, pre, v) finishes and stores.  A tile epilogue issues pre() for
 // many groups before the first put(), so their loads are in flight together
-// instead of one load-use-store round trip per group.
+// instead of one load-use-store round trip per group.  row(m) is also
+// available as row_from(m, row_key(m)), where row_key(m) is the one per-row
+// value read from memory (0 when there is none), so that a tile can load the
+// keys of all its rows at once and share them between lanes.
 // ---------------------------------------------------------------------------
 
 // out[m, n] = acc (stored in TO)
@@ -46,8 +49,11 @@ struct EpiStore {
   TO* out;
   int ldo;
   using Row = int64_t;
+  static constexpr bool kRowKey = false;
   __device__ __forceinline__ bool vec_ok() const { return (ldo & 3) == 0; }
   __device__ __forceinline__ Row row(int m) const { return static_cast<int64_t>(m) * ldo; }
+  __device__ __forceinline__ int row_key(int) const { return 0; }
+  __device__ __forceinline__ Row row_from(int m, int) const { return row(m); }
   __device__ __forceinline__ f32x4 pre(Row, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
   __device__ __forceinline__ void put(Row r, int n, f32x4, const float v[4]) const {
     Vec4<TO>::store(out + r + n, v);
@@ -69,8 +75,11 @@ struct EpiResid {
   const TR* resid;
   int ldo;
   using Row = int64_t;
+  static constexpr bool kRowKey = false;
   __device__ __forceinline__ bool vec_ok() const { return (ldo & 3) == 0; }
   __device__ __forceinline__ Row row(int m) const { return static_cast<int64_t>(m) * ldo; }
+  __device__ __forceinline__ int row_key(int) const { return 0; }
+  __device__ __forceinline__ Row row_from(int m, int) const { return row(m); }
   __device__ __forceinline__ f32x4 pre(Row r, int n) const {
     float t[4];
     Vec4<TR>::load(resid + r + n, t);
@@ -129,16 +138,20 @@ struct EpiQkv {
     int64_t kv_row;  // row of k / v (cache slot row when kv_cap > 0)
     int pos;         // rotation position
   };
+  static constexpr bool kRowKey = true;
   __device__ __forceinline__ bool vec_ok() const {
     return (hd & 3) == 0 && (nq_hd & 3) == 0 && (nkv_hd & 3) == 0;
   }
-  __device__ __forceinline__ Row row(int m) const {
+  // the per-token value a row needs from memory (its position), and the row built from it
+  __device__ __forceinline__ int row_key(int m) const { return positions[m]; }
+  __device__ __forceinline__ Row row_from(int m, int pos) const {
     Row r;
     r.m = m;
-    r.pos = positions[m];
-    r.kv_row = kv_cap > 0 ? static_cast<int64_t>(m / seq_len) * kv_cap + r.pos : static_cast<int64_t>(m);
+    r.pos = pos;
+    r.kv_row = kv_cap > 0 ? static_cast<int64_t>(m / seq_len) * kv_cap + pos : static_cast<int64_t>(m);
     return r;
   }
+  __device__ __forceinline__ Row row(int m) const { return row_from(m, row_key(m)); }
   // (cos, sin) of the group's two pairs (unused for V columns)
   __device__ __forceinline__ f32x4 pre(const Row& r, int n) const {
     if (n >= nq_hd + nkv_hd) return f32x4{1.f, 0.f, 1.f, 0.f};
