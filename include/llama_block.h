@@ -39,6 +39,10 @@
  *   nothing is enqueued and llama_last_error() holds a thread-local message.
  *   Faults inside a kernel surface at the caller's next synchronization.
  *   No C++ exception crosses this ABI.
+ * Empty problems: a count of rows, tokens or sequences equal to 0 is a valid
+ *   empty call; it returns LLAMA_OK, enqueues nothing and writes nothing.
+ *   Negative counts and zero widths (d_model, head_dim, d_ff, head counts,
+ *   vocab, cache capacity) are LLAMA_ERR_INVALID_ARGUMENT.
  */
 #ifndef LLAMA_BLOCK_H
 #define LLAMA_BLOCK_H
@@ -56,7 +60,7 @@ enum llama_dtype { LLAMA_F32 = 0, LLAMA_BF16 = 1 };
 
 enum llama_status {
   LLAMA_OK = 0,
-  LLAMA_ERR_INVALID_ARGUMENT = -1,    /* null pointer, non-positive size, n_q % n_kv != 0, odd head_dim, ... */
+  LLAMA_ERR_INVALID_ARGUMENT = -1,    /* null pointer, negative count, zero width, n_q % n_kv != 0, odd head_dim, ... */
   LLAMA_ERR_UNSUPPORTED = -2,         /* valid but not handled (dtype code, head_dim > 256, misaligned pointer) */
   LLAMA_ERR_WORKSPACE_TOO_SMALL = -3, /* ws_bytes below the matching *_workspace_bytes() */
   LLAMA_ERR_HIP = -4                  /* a HIP launch reported an error */

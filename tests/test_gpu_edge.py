@@ -1,0 +1,98 @@
+"""Empty problems on the GPU: every entry point accepts a call with zero rows,
+tokens or sequences, returns LLAMA_OK and writes nothing (the output buffers
+keep a sentinel).  Zero-row views of real buffers keep every pointer valid.
+Needs a GPU."""
+
+import pytest
+import torch
+
+from llama_decoder_block_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SENTINEL = -7.25
+
+
+def filled(shape, dtype=torch.float32):
+    return torch.full(shape, SENTINEL, dtype=dtype, device=DEV)
+
+
+def unchanged(t):
+    if t.dtype == torch.uint8:
+        return bool(torch.all(t == 0xA5))
+    if t.dtype == torch.int32:
+        return bool(torch.all(t == -3))
+    return bool(torch.all(t == SENTINEL))
+
+
+def test_rmsnorm_and_rope_empty():
+    x = filled((8, 256))
+    gamma = torch.ones(256, dtype=torch.bfloat16, device=DEV)
+    out = filled((8, 256), torch.bfloat16)
+    binding.rmsnorm(x[:0], gamma, 1e-5, out=out[:0])
+    q = filled((8, 4, 64), torch.bfloat16)
+    k = filled((8, 2, 64), torch.bfloat16)
+    pos = torch.zeros(8, dtype=torch.int32, device=DEV)
+    binding.rope(q[:0], k[:0], pos[:0], 1e4)
+    torch.cuda.synchronize()
+    assert unchanged(out) and unchanged(q) and unchanged(k)
+
+
+@pytest.mark.parametrize("shape", [(0, 5), (2, 0)])
+def test_attention_empty(shape):
+    """No sequences, or sequences with no query tokens."""
+    B, Tq = shape
+    q = filled((2, 5, 4, 128), torch.bfloat16)
+    kv = filled((2, 16, 2, 128), torch.bfloat16)
+    out = filled((2, 5, 4, 128), torch.bfloat16)
+    binding.gqa_attention(q[:B, :Tq], kv[:B], kv[:B], out=out[:B, :Tq])
+    torch.cuda.synchronize()
+    assert unchanged(out)
+
+
+def test_swiglu_and_block_empty():
+    wl = synth.workload("llama3_8b_gqa_prefill", seq=4, d_model=256, n_q=4, n_kv=2, head_dim=64, d_ff=512)
+    inp = synth.make_block_inputs(wl)
+    w = {n: t.to(DEV) for n, t in inp.weights.items()}
+    res = filled((4, 256))
+    out = filled((4, 256))
+    binding.swiglu_ffn(res[:0].to(torch.bfloat16), w["w_gate"], w["w_up"], w["w_down"], residual=res[:0],
+                       out=out[:0])
+    x = filled((1, 4, 256))
+    y = filled((1, 4, 256))
+    pos = torch.arange(4, dtype=torch.int32, device=DEV).reshape(1, 4)
+    binding.block_forward(x[:, :0], w, pos[:, :0], 4, 2, 1e4, 1e-5, y=y[:, :0])    # no tokens
+    binding.block_forward(x[:0], w, pos[:0], 4, 2, 1e4, 1e-5, y=y[:0])             # no sequences
+    torch.cuda.synchronize()
+    assert unchanged(out) and unchanged(y)
+
+
+def test_cache_writers_empty():
+    k = filled((2, 3, 8, 128), torch.bfloat16)
+    pos = torch.zeros(2, 3, dtype=torch.int32, device=DEV)
+    k8, v8, ks, vs = binding.fp8_cache(2, 16, 8, 128, DEV)
+    for t in (k8, v8):
+        t.fill_(0xA5)
+    for t in (ks, vs):
+        t.fill_(SENTINEL)
+    binding.kv_append_fp8(k[:, :0], k[:, :0], pos[:, :0], k8, v8, ks, vs)
+    pages = filled((4, 64, 8, 128), torch.bfloat16)
+    table = torch.arange(4, dtype=torch.int32, device=DEV).reshape(2, 2)
+    binding.kv_append_paged(k[:, :0], k[:, :0], pos[:, :0], table, pages, pages)
+    torch.cuda.synchronize()
+    assert all(unchanged(t) for t in (k8, v8, ks, vs, pages))
+
+
+def test_lm_head_empty():
+    h = filled((4, 256))
+    gamma = torch.ones(256, dtype=torch.bfloat16, device=DEV)
+    w = filled((1000, 256), torch.bfloat16)
+    token = torch.full((4,), -3, dtype=torch.int32, device=DEV)
+    logits = filled((4, 1000))
+    best = filled((4,))
+    L = binding.lib()
+    rc = L.llama_lm_head_argmax(h.data_ptr(), gamma.data_ptr(), w.data_ptr(), token.data_ptr(), logits.data_ptr(),
+                                best.data_ptr(), 0, 256, 1000, 1e-5, binding.BF16, binding.F32, None, 0, None)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert unchanged(token) and unchanged(logits) and unchanged(best)
