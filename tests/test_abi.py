@@ -240,3 +240,22 @@ def test_lm_head_validation():
                                   None) == -3
     assert L.llama_lm_head_argmax(FAKE, FAKE, FAKE, FAKE + 4, None, None, 64, 4096, 128256, 1e-5, 1, 0, FAKE, need,
                                   None) == -2                     # misaligned
+
+
+def test_zero_widths_are_invalid():
+    """Zero widths fail validation on the host; the empty-call contract (zero
+    counts succeed and write nothing) is checked on the GPU."""
+    L = binding.lib()
+    bad = [
+        L.llama_rmsnorm(FAKE, None, FAKE, FAKE + 0x100, None, 4, 0, 1e-5, 1, 0, None),
+        L.llama_rope(FAKE, FAKE + 0x100, FAKE + 0x200, 4, 4, 2, 0, 1e4, 1, None),
+        L.llama_gqa_attention(FAKE, FAKE + 0x100, FAKE + 0x200, FAKE + 0x300, None, 1, 4, 0, 4, 2, 64, 1, None, 0,
+                              None),
+        L.llama_gqa_attention(FAKE, FAKE + 0x100, FAKE + 0x200, FAKE + 0x300, None, 1, 4, 8, 0, 2, 64, 1, None, 0,
+                              None),
+        L.llama_swiglu_ffn(FAKE, FAKE, FAKE, FAKE, None, FAKE + 0x100, 4, 0, 64, 1, 0, None, 0, None),
+        L.llama_swiglu_ffn(FAKE, FAKE, FAKE, FAKE, None, FAKE + 0x100, 4, 64, 0, 1, 0, None, 0, None),
+        L.llama_lm_head_argmax(FAKE, FAKE, FAKE, FAKE + 0x100, None, None, 4, 64, 0, 1e-5, 1, 0, None, 0, None),
+        L.llama_lm_head_argmax(FAKE, FAKE, FAKE, FAKE + 0x100, None, None, 4, 0, 100, 1e-5, 1, 0, None, 0, None),
+    ]
+    assert all(rc == -1 for rc in bad), bad
