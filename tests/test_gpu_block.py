@@ -278,3 +278,29 @@ def test_decode_step_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(y_graph, y_eager), f"replay {i}"
         del junk
+
+
+@pytest.mark.parametrize("seq", [300, 1])
+def test_block_on_a_side_stream(seq):
+    """The library enqueues on the caller's stream: the block run on a second
+    stream (default priority) gives the default-stream result bit for bit,
+    for a prefill and for a decode step against a cache."""
+    if seq == 1:
+        wl = synth.workload("llama3_8b_gqa_decode", batch=5, d_model=512, n_q=8, n_kv=2, head_dim=128, d_ff=1376,
+                            decode_pos=70, kv_cap=96)
+    else:
+        wl = small_bf16(seq=seq)
+    inp = synth.make_block_inputs(wl)
+    x, w, pos, kc, vc = to_dev(inp)
+    caches = lambda: (kc.clone() if kc is not None else None, vc.clone() if vc is not None else None)
+    k0, v0 = caches()
+    k1, v1 = caches()
+    y0 = binding.block_forward(x, w, pos, wl.n_q, wl.n_kv, wl.theta, wl.eps, k_cache=k0, v_cache=v0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        y1 = binding.block_forward(x, w, pos, wl.n_q, wl.n_kv, wl.theta, wl.eps, k_cache=k1, v_cache=v1)
+    side.synchronize()
+    assert torch.equal(y0, y1)
+    if k0 is not None:
+        assert torch.equal(k0, k1) and torch.equal(v0, v1)
