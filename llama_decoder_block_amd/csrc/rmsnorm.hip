@@ -7,6 +7,8 @@
 // reduced across the wavefront with butterfly shuffles and across the four
 // wavefronts through LDS.  HBM-bound: each element is read once and written
 // once; the row stays in registers between the reduction and the scaling.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -70,6 +72,50 @@ rmsnorm_vec_kernel(const TR* __restrict__ x, const TR* __restrict__ res,
   }
 }
 
+// Wavefront path (d = 256 * 2^k up to 8192): one wavefront per row,
+// four rows per workgroup.  Each lane holds d/64 elements as V chunks of
+// four (a wavefront load covers 256 contiguous elements), so every lane has V
+// loads in flight at once and the sum of squares needs only the wavefront's
+// own butterfly, no LDS and no barrier.
+template <typename TR, typename TO, int V>
+__global__ void __launch_bounds__(kNormThreads)
+rmsnorm_wave_kernel(const TR* __restrict__ x, const TR* __restrict__ res,
+                    const TO* __restrict__ gamma, TO* __restrict__ out, TR* sum_out,
+                    int64_t rows, int d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kNormThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t base = row * d;
+  float v[V][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < V; ++c) Vec4<TR>::load(x + base + 4 * (lane + 64 * c), v[c]);
+  if (res) {
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+      float r[4];
+      Vec4<TR>::load(res + base + 4 * (lane + 64 * c), r);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[c][e] += r[e];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < V; ++c) {
+    if (sum_out) Vec4<TR>::store(sum_out + base + 4 * (lane + 64 * c), v[c]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += v[c][e] * v[c][e];
+  }
+  const float inv = rsqrtf(wave_sum(ss) / static_cast<float>(d) + eps);
+#pragma unroll
+  for (int c = 0; c < V; ++c) {
+    float g[4], o[4];
+    Vec4<TO>::load(gamma + 4 * (lane + 64 * c), g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = v[c][e] * inv * g[e];
+    Vec4<TO>::store(out + base + 4 * (lane + 64 * c), o);
+  }
+}
+
 // Generic path: any d; the second pass re-reads the row (L2-resident).
 template <typename TR, typename TO>
 __global__ void __launch_bounds__(kNormThreads)
@@ -104,6 +150,23 @@ hipError_t launch_rmsnorm_t(const void* x, const void* res, const void* gamma, v
   TR* sp = static_cast<TR*>(sum_out);
   dim3 grid(static_cast<unsigned>(rows)), block(kNormThreads);
   const bool vec = (d % 4 == 0);
+  const int per_lane = d % 256 == 0 ? d / 256 : 0;  // 4-element chunks per lane on the wavefront path
+  if (per_lane == 1 || per_lane == 2 || per_lane == 4 || per_lane == 8 || per_lane == 16 || per_lane == 32) {
+    const dim3 wgrid(static_cast<unsigned>((rows + 3) / 4));
+    auto go = [&](auto vc) {
+      constexpr int V = decltype(vc)::value;
+      hipLaunchKernelGGL((rmsnorm_wave_kernel<TR, TO, V>), wgrid, block, 0, s, xp, rp, gp, op, sp, rows, d, eps);
+    };
+    switch (per_lane) {
+      case 1: go(std::integral_constant<int, 1>{}); break;
+      case 2: go(std::integral_constant<int, 2>{}); break;
+      case 4: go(std::integral_constant<int, 4>{}); break;
+      case 8: go(std::integral_constant<int, 8>{}); break;
+      case 16: go(std::integral_constant<int, 16>{}); break;
+      default: go(std::integral_constant<int, 32>{}); break;
+    }
+    return hipGetLastError();
+  }
   const int chunks_per_thread = (d / 4 + kNormThreads - 1) / kNormThreads;
   if (vec && chunks_per_thread <= 2)
     hipLaunchKernelGGL((rmsnorm_vec_kernel<TR, TO, 2>), grid, block, 0, s, xp, rp, gp, op, sp, d, eps);
