@@ -240,6 +240,100 @@ def bench_rope(wl, dev, args):
             "kernel_avg_us": round(avg_us, 2)}
 
 
+def seeded_cache(shape, seed, dev):
+    """bf16 K or V cache drawn on the GPU from N(0, 1) with a seeded generator."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+
+def bench_chunked_prefill(wl, dev, args, history=24576):
+    """A prefill chunk against an existing cache: the workload's 8192 tokens at
+    positions history..history+8191, attending the `history` cached slots and
+    themselves (causally), through the block entry point with the cache."""
+    inp = synth.make_block_inputs(wl)
+    w = {k: v.to(dev) for k, v in inp.weights.items()}
+    x = inp.x.to(dev)
+    B, T = wl.batch, wl.seq
+    cap = history + T
+    pos = (history + torch.arange(T, dtype=torch.int32)).repeat(B, 1).to(dev)
+    kc = seeded_cache((B, cap, wl.n_kv, wl.head_dim), 1000 * wl.index + 60, dev)
+    vc = seeded_cache((B, cap, wl.n_kv, wl.head_dim), 1000 * wl.index + 61, dev)
+    need = binding.block_workspace_bytes(B, T, wl.d_model, wl.n_q, wl.n_kv, wl.head_dim, wl.d_ff, cap,
+                                         binding.BF16, binding.F32)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+
+    def step():
+        binding.block_forward(x, w, pos, wl.n_q, wl.n_kv, wl.theta, wl.eps, k_cache=kc, v_cache=vc, y=y,
+                              workspace=ws)
+    ms, per, kernels = time_steps(step, args.steps, args.warmup)
+    sh = shape_of(wl)
+    att = wm.chunk_attention_flops(sh, B, T, history)
+    flops = wm.prefill_linear_flops(sh, B * T) + att
+    n_at, ms_at = kernels.get("attention/attn_flash_prefill", (0, 0.0))
+    at_us = ms_at / max(n_at, 1) * 1e3
+    log(f"[bench] chunked prefill ({T} tokens after {history} cached): {ms:.3f} ms/step, "
+        f"{flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s; attention {at_us:.1f} us = {att / (at_us * 1e-6) / 1e12:.1f} TFLOP/s")
+    out = {"workload": f"{PREFILL} tokens as one chunk at positions {history}..{cap - 1} against a bf16 cache of "
+                       f"{history} earlier slots [{B},{cap},{wl.n_kv},{wl.head_dim}]",
+           "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "attention": {"avg_us": round(at_us, 2), "flops": att,
+                         "tflops": round(att / (at_us * 1e-6) / 1e12, 1) if n_at else None},
+           "kernels": kernel_table(kernels, wm.step_work(sh, B, T))}
+    del step, w, x, kc, vc, ws, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_long_decode(wd, dev, args, batch=8, position=32767):
+    """The decode step for `batch` sequences at `position` (a 32K-slot cache):
+    few (sequence, KV head) pairs, so decode attention splits each history
+    over workgroups and merges the chunks."""
+    small = synth.workload(DECODE, batch=batch, decode_pos=0, kv_cap=1)
+    inp = synth.make_block_inputs(small)
+    w = {k: v.to(dev) for k, v in inp.weights.items()}
+    x = inp.x.to(dev)
+    cap = position + 1
+    kc = seeded_cache((batch, cap, wd.n_kv, wd.head_dim), 1000 * wd.index + 70, dev)
+    vc = seeded_cache((batch, cap, wd.n_kv, wd.head_dim), 1000 * wd.index + 71, dev)
+    pos = torch.full((batch, 1), position, dtype=torch.int32, device=dev)
+    need = binding.block_workspace_bytes(batch, 1, wd.d_model, wd.n_q, wd.n_kv, wd.head_dim, wd.d_ff, cap,
+                                         binding.BF16, binding.F32)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+
+    def step():
+        binding.block_forward(x, w, pos, wd.n_q, wd.n_kv, wd.theta, wd.eps, k_cache=kc, v_cache=vc, y=y,
+                              workspace=ws)
+    scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    dms, _, dk = time_steps(step, args.decode_steps, args.warmup, flush=lambda: scratch.sum())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    gms, gper, _ = time_steps(graph.replay, args.decode_steps, args.warmup, flush=lambda: scratch.sum())
+    del scratch, graph
+    sh = shape_of(wd)
+    at_bytes = wm.decode_attention_bytes(sh, batch, cap)
+    name = next((k for k in dk if k.startswith("attention/")), None)
+    n_at, ms_at = dk.get(name, (0, 0.0))
+    at_us = ms_at / max(n_at, 1) * 1e3
+    gbs = at_bytes / (at_us * 1e-6) / 1e9 if n_at else 0.0
+    log(f"[bench] long-context decode ({batch} sequences at position {position}): {gms * 1e3:.1f} us/step in a "
+        f"graph; attention ({name}) {at_us:.1f} us = {gbs:.0f} GB/s")
+    out = {"workload": f"{DECODE} step for {batch} sequences at position {position}, bf16 cache "
+                       f"[{batch},{cap},{wd.n_kv},{wd.head_dim}], last-level cache flushed between steps",
+           "ms_per_step": round(gms, 4), "tokens_per_s": round(batch / (gms * 1e-3), 1),
+           "eager_ms_per_step": round(dms, 4),
+           "attention": {"kernel": name, "bound": "hbm", "avg_us": round(at_us, 2), "bytes": at_bytes,
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    del step, w, x, kc, vc, ws, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode_fp8kv(wd, dev, args):
     """The decode workload against an 8-bit KV cache (E4M3 codes + one fp32
     scale per row) holding the same synthetic history, quantized on the GPU by
@@ -434,6 +528,7 @@ def main():
     del step
     torch.cuda.empty_cache()
     rope = bench_rope(wl, dev, args)
+    chunked = bench_chunked_prefill(wl, dev, args)
 
     # ---------------- decode -----------------
     decode = None
@@ -490,6 +585,7 @@ def main():
         decode["fp8kv"] = bench_decode_fp8kv(wd, dev, args)
         decode["paged_attention"] = bench_paged_attention(wd, dev, args)
         decode["lm_head"] = bench_lm_head(wd, dev, args)
+        decode["long_context"] = bench_long_decode(wd, dev, args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -523,6 +619,7 @@ def main():
                      "flops_per_launch": dom_flops, "avg_us": round(dom_avg_ms * 1e3, 2)},
         "kernels": table,
         "rope": rope,
+        "chunked_prefill": chunked,
         "decode": decode,
         "device": device,
         "hbm_copy": copy_bw,

@@ -56,6 +56,12 @@ def prefill_attention_flops(s, batch, seq):
     return 4 * s.head_dim * s.n_q * causal_pairs(batch, seq)
 
 
+def chunk_attention_flops(s, batch, seq, start):
+    """A chunk of `seq` tokens at positions start..start+seq-1 against a cache
+    holding the `start` earlier ones: token i sees start + i + 1 slots."""
+    return 4 * s.head_dim * s.n_q * batch * (seq * start + seq * (seq + 1) // 2)
+
+
 def dense_attention_flops(s, batch, seq):
     return 4 * s.head_dim * s.n_q * batch * seq * seq
 

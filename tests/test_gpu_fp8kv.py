@@ -131,11 +131,11 @@ def kernel_used(fn):
 
 @pytest.mark.parametrize("nq,nkv", [(32, 8), (8, 8), (16, 8), (32, 4), (64, 8)])
 def test_decode_attention_fp8kv(nq, nkv):
-    """Ragged visible lengths over 32 sequences (one workgroup per pair)."""
-    B, S, hd = 32, 700, 128
+    """Ragged visible lengths over 48 sequences (one workgroup per pair)."""
+    B, S, hd = 48, 700, 128
     kc, vc, ks, vs = quantized_cache(220, B, S, nkv, hd)
     lens = [700, 1, 33, 64, 65, 300, 511, 512, 513, 699, 2, 31, 32, 100, 257, 640, 7, 650, 690, 350, 128, 129, 96, 97,
-            3, 63, 95, 160, 191, 224, 400, 555]
+            3, 63, 95, 160, 191, 224, 400, 555, 16, 17, 48, 49, 80, 81, 200, 256, 384, 448, 449, 600, 601, 666, 698, 5]
     pos = np.array([n - 1 for n in lens])
     kd, vd = fp8.kv_cache_values(kc, ks), fp8.kv_cache_values(vc, vs)
     poison_unwritten(kc, vc, ks, vs, pos)

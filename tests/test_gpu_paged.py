@@ -75,16 +75,16 @@ def test_append_paged_places_rows():
 
 @pytest.mark.parametrize("nq,nkv,P", [(32, 8, 64), (8, 8, 32), (32, 4, 128), (64, 8, 64)])
 def test_decode_attention_paged(nq, nkv, P):
-    """32 sequences with ragged visible lengths over shuffled pages of a pool
-    whose other rows are NaN."""
-    B, hd = 32, 128
+    """48 sequences with ragged visible lengths over shuffled pages of a pool
+    whose other rows are NaN (one workgroup per (sequence, KV head))."""
+    B, hd = 48, 128
     max_pages = -(-700 // P)
     n_pages = B * max_pages + 7
     S = max_pages * P
     k = synth.normal(310, (B, S, nkv, hd), dtype="bf16")
     v = synth.normal(311, (B, S, nkv, hd), dtype="bf16")
     lens = [700, 1, 33, 64, 65, 300, 511, 512, 513, 699, 2, 31, 32, 100, 257, 640, 7, 650, 690, 350, 128, 129, 96, 97,
-            3, 63, 95, 160, 191, 224, 400, 555]
+            3, 63, 95, 160, 191, 224, 400, 555, 16, 17, 48, 49, 80, 81, 200, 256, 384, 448, 449, 600, 601, 666, 698, 5]
     pos = np.array([n - 1 for n in lens])
     table = shuffled_table(312, B, max_pages, n_pages)
     kc, vc = to64(k), to64(v)

@@ -62,3 +62,14 @@ def test_fp8_kv_bytes_halve_the_cache_plus_row_scales():
     assert b8 == b16 // 2 + 64 * 4097 * 2 * 8 * 4
     w = wm.step_work(L3_8B, 64, 1, attend_len=4097, kv_bytes=wm.FP8KV_BYTES_PER_ELEM)
     assert w["attention"][1] == b8
+
+
+def test_chunk_attention_flops():
+    """A chunk at position 0 is a plain causal prefill; a one-token chunk at
+    position p is a decode step attending p + 1 slots; two consecutive chunks
+    add up to the prefill of their union."""
+    s = wm.Shape(4096, 32, 8, 128, 14336)
+    assert wm.chunk_attention_flops(s, 2, 8192, 0) == wm.prefill_attention_flops(s, 2, 8192)
+    assert wm.chunk_attention_flops(s, 64, 1, 4096) == wm.decode_attention_flops(s, 64, 4097)
+    assert (wm.chunk_attention_flops(s, 1, 3000, 0) + wm.chunk_attention_flops(s, 1, 5192, 3000)
+            == wm.prefill_attention_flops(s, 1, 8192))
