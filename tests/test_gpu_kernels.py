@@ -316,16 +316,18 @@ def test_decode_attention_few_sequences_long_cache():
     assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, to64(v)))
 
 
-def test_decode_attention_long_context():
-    """One sequence at position 32768 against a 32769-slot cache (Llama-3-8B
-    heads): the split over workgroups with a merge through the workspace."""
-    B, S, nq, nkv, hd = 1, 32769, 32, 8, 128
+@pytest.mark.parametrize("S", [32769, 131072])
+def test_decode_attention_long_context(S):
+    """One sequence at the last position of a 32769- or 131072-slot cache
+    (Llama-3-8B heads; the pages tabulate caches out to about 128K tokens):
+    the split over workgroups with a merge through the workspace."""
+    B, nq, nkv, hd = 1, 32, 8, 128
     q, k, v = attn_inputs(97, B, 1, S, nq, nkv, hd, "bf16")
     pos = torch.tensor([[S - 1]], dtype=torch.int32)
     out, used = decode_kernel_used(q, k, v, pos)
     assert used == ["attention/attn_decode_splitk"]
     ref = oracle.gqa_attention(to64(q), to64(k), to64(v), to64(pos).astype(np.int64))
-    report("decode 32K", out, ref)
+    report(f"decode {S} slots", out, ref)
     assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, to64(v)))
 
 
