@@ -813,7 +813,10 @@ attn_decode2_kernel(AttnArgs a, int n_chunks, int chunk_len, float* __restrict__
   using St = DecState<R>;
   __shared__ float s_p[4][SUB][St::RP];   // weights [slot][query] per wavefront
   __shared__ float s_alpha[4][St::RP];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wavefront index made visibly uniform: the task, and with it the
+  // buffer resources of the 8-bit cache rows, derive from it (a per-lane
+  // resource would wrap every load in a read-first-lane loop)
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int task = blockIdx.x * 4 + w;
   if (task >= a.B * a.nkv * n_chunks) return;
   const int chunk = task % n_chunks;

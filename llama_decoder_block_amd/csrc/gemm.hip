@@ -227,31 +227,6 @@ gemm_mfma_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, in
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel, large tiles: 256 x 256 output tile, eight wavefronts (two per
-// SIMD, so one wavefront's LDS and memory waits overlap the other's MFMAs).
-// Wave grid 2 (N) x 4 (M); each wavefront owns 128 (N) x 64 (M) as 4 x 2
-// tiles of 32 x 32.  Requires K % 64 == 0 (no K tail) so that the global
-// loads of the next K step are issued unconditionally; rows past M or N are
-// clamped on load and dropped by the epilogue.  Fragments of the next
-// 16-wide K slice are read from LDS while the current slice's MFMAs run.
-// ---------------------------------------------------------------------------
-// MFMA kernel, large tiles, direct-to-LDS staging ("dma" kernel).
-// 256 x 256 output tile, four wavefronts (one per SIMD) in a 2 x 2 grid, each
-// owning 128 x 128 as 4 x 4 tiles of 32 x 32 (accumulators in AGPRs).
-// K advances in stages of 32.  Global memory is copied straight into LDS by
-// global_load_lds_dwordx4 (lane l of an instruction writes LDS bytes
-// M0 + 16 l .. +15), so no registers stage the tiles; NST stage buffers let
-// the copies of stage kt+NST-1 be issued while stage kt computes.
-// LDS rows are 64 B (32 bf16): chunk c of row r is stored at chunk
-// c ^ ((r / 4) % 4), which keeps the 16 lanes served together by a 16-byte
-// LDS read (16 consecutive rows, one chunk) on 16 distinct bank groups; the
-// copy realises the swizzle by choosing each lane's global chunk.
-// Inside a stage the fragments of the next 16-wide sub-step are read while
-// the current sub-step's 16 MFMAs run, and the first fragments of stage kt+1
-// are read before the end-of-stage barrier (that stage was confirmed complete
-// one barrier earlier), so the barrier does not idle the matrix cores.
-// Requires K % 32 == 0.
-// ---------------------------------------------------------------------------
 // MFMA kernel, large tiles, register-staged buffer loads ("rs" kernel).
 // 256 x 256 output tile, four wavefronts (one per SIMD) in a 2 x 2 grid, each
 // owning 128 x 128 as 4 x 4 tiles of 32 x 32 (accumulators in AGPRs).
@@ -703,7 +678,10 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
   // per wavefront: 64 weight rows + 64 token rows of one step (128 B each);
   // reused afterwards for the cross-wavefront sum
   __shared__ u32x4 lds[4][2][64 * 8];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The wavefront index is made visibly uniform: the K offsets derived from
+  // it are the buffer loads' scalar offsets, which would otherwise be taken
+  // for per-lane values and every load wrapped in a read-first-lane loop.
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t row_bytes = static_cast<uint32_t>(K) * 2u;
 
   // buffer resources of the two 32-row weight blocks of this workgroup
@@ -723,7 +701,9 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
       base = op.w[seg] + static_cast<int64_t>(r0 - start) * K;
       left = op.wrows[seg] - (r0 - start);
     }
-    left = max(0, min(left, 32));
+    // clamped on the vector unit (no scalar min/max of three), hence made
+    // visibly uniform again, like the wavefront index above
+    left = __builtin_amdgcn_readfirstlane(max(0, min(left, 32)));
     wr[fb] = make_rsrc(base, static_cast<uint32_t>(left) * row_bytes);
   }
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, static_cast<uint32_t>(M) * row_bytes);
@@ -840,7 +820,7 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
 // ---------------------------------------------------------------------------
 struct Plan {
   bool mfma;
-  bool big;       // 256x256 eight-wave kernel
+  bool big;       // 256x256 four-wave kernel (gemm_mfma_rs_kernel)
   int bn, bm;     // MFMA tile (bn = weight rows per tile incl. both halves when dual)
   int splits;     // K splits (>1: partial sums + reduce)
   int k_per_split;
