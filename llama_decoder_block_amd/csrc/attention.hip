@@ -134,9 +134,13 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kFBufBytes];
   __shared__ int vis_s[kFRows];
 
-  // heavy tiles (late query tokens) first
-  const int qt = n_qtiles - 1 - static_cast<int>(blockIdx.x % n_qtiles);
-  const int bg = blockIdx.x / n_qtiles;
+  // Heavy tiles (late query tokens) first across all (sequence, KV group)
+  // pairs, so the last workgroups to start are the light ones; consecutive
+  // workgroups take consecutive pairs, so with workgroups placed on the XCDs
+  // in turn each XCD's L2 serves few KV heads.
+  const int n_bg = static_cast<int>(gridDim.x) / n_qtiles;
+  const int qt = n_qtiles - 1 - static_cast<int>(blockIdx.x) / n_bg;
+  const int bg = static_cast<int>(blockIdx.x) % n_bg;
   const int g = bg % a.nkv, b = bg / a.nkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t0 = qt * TQ;
