@@ -144,25 +144,7 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
   const int g = bg % a.nkv, b = bg / a.nkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t0 = qt * TQ;
-
-  if (tid < kFRows) {
-    const int t = t0 + tid % TQ;
-    int vis = -1;
-    if (t < a.Tq) vis = a.positions ? a.positions[static_cast<int64_t>(b) * a.Tq + t] : t;
-    vis_s[tid] = vis;
-  }
-  __syncthreads();
-  int maxvis = -1;
-  for (int i = 0; i < kFRows; ++i) maxvis = max(maxvis, vis_s[i]);
   const int my_row = w * 32 + (lane & 31);
-  const int my_vis = vis_s[my_row];
-  int wave_min = 0x7fffffff;
-  for (int i = 0; i < 32; ++i) {
-    const int v = vis_s[w * 32 + i];
-    wave_min = min(wave_min, v < 0 ? 0x7fffffff : v);
-  }
-  const int nkt = maxvis < 0 ? 0 : maxvis / kFKeys + 1;
-
   const int my_hi = my_row / TQ, my_t = t0 + my_row % TQ;
   const int my_h = g * R + my_hi;
   const int half = lane >> 5;
@@ -176,12 +158,30 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + half * 8);
-    // Consume the Q fragments here, so their loads are complete before the
-    // tile loop: otherwise the wait for them is placed inside the loop, where
-    // (the counter being in order) it also waits for the next tile's K/V.
+    // Consume the Q fragments before the tile loop, so their wait is not
+    // placed inside it, where (the counter being in order) it would also
+    // wait for the next tile's K/V.  Issued first, they share the latency of
+    // the position loads below.
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(qf[kk]));
   }
+
+  if (tid < kFRows) {
+    const int t = t0 + tid % TQ;
+    int vis = -1;
+    if (t < a.Tq) vis = a.positions ? a.positions[static_cast<int64_t>(b) * a.Tq + t] : t;
+    vis_s[tid] = vis;
+  }
+  __syncthreads();
+  int maxvis = -1;
+  for (int i = 0; i < kFRows; ++i) maxvis = max(maxvis, vis_s[i]);
+  const int my_vis = vis_s[my_row];
+  int wave_min = 0x7fffffff;
+  for (int i = 0; i < 32; ++i) {
+    const int v = vis_s[w * 32 + i];
+    wave_min = min(wave_min, v < 0 ? 0x7fffffff : v);
+  }
+  const int nkt = maxvis < 0 ? 0 : maxvis / kFKeys + 1;
 
   const int64_t kvrow = static_cast<int64_t>(a.nkv) * kFHd;  // elements between slots
   const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * kFHd;
