@@ -195,6 +195,21 @@ def test_flash_bf16(nq, nkv, T):
     assert np.all(err <= attention_bound(ref, to64(v))), err.max()
 
 
+def test_flash_bf16_every_tile_written_once():
+    """Workgroup numbering of the flash kernel: three sequences and four KV
+    heads (12 (sequence, KV head) pairs, not a power of two) and a ragged last
+    query tile.  The output starts as NaN, so a tile that no workgroup writes
+    fails the bound."""
+    B, T, nq, nkv, hd = 3, 200, 8, 4, 128
+    q, k, v = attn_inputs(51, B, T, T, nq, nkv, hd, "bf16")
+    out = torch.full((B, T, nq, hd), float("nan"), dtype=torch.bfloat16, device="cuda")
+    binding.gqa_attention(dev(q), dev(k), dev(v), out=out)
+    torch.cuda.synchronize()
+    ref = oracle.gqa_attention(to64(q), to64(k), to64(v), np.broadcast_to(np.arange(T), (B, T)))
+    report("flash bf16 3 sequences", out, ref)
+    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, to64(v)))
+
+
 def test_flash_bf16_positions_with_cache():
     # prefill of a chunk against a longer cache: queries at positions 100..163
     B, T, S, nq, nkv, hd = 2, 64, 300, 8, 2, 128
