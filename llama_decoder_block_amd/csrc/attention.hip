@@ -118,15 +118,6 @@ constexpr int kKBytes = kFKeys * kKStride;
 constexpr int kVBytes = kFHd * kVStride;
 constexpr int kFBufBytes = kKBytes + kVBytes;
 
-#ifndef LB_FLASH_PRIO
-#define LB_FLASH_PRIO 0
-#endif
-#if LB_FLASH_PRIO
-#define FLASH_PRIO(p) __builtin_amdgcn_s_setprio(p)
-#else
-#define FLASH_PRIO(p) ((void)0)
-#endif
-
 template <int R>
 __global__ void __launch_bounds__(256, 2)
 attn_flash_kernel(AttnArgs a, int n_qtiles) {
@@ -277,7 +268,6 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.f;
-    FLASH_PRIO(1);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
@@ -286,7 +276,6 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
             kb + (h2 * 32 + (lane & 31)) * kKStride + kk * 32 + half * 16);
         sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[h2], 0, 0, 0);
       }
-    FLASH_PRIO(0);
     // Raw-score maximum of the tile (the scale c > 0 preserves order); keys
     // past a query's position are masked only on tiles that reach the
     // diagonal of some row of this wavefront (wave-uniform test).
@@ -343,7 +332,6 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
     l_run += psum;
 
     // O^T += V^T P^T
-    FLASH_PRIO(1);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -357,7 +345,6 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
                                                             pf[h2][hh], oacc[d], 0, 0, 0);
         }
       }
-    FLASH_PRIO(0);
     if (kt + 1 < nkt) lstore(buf ^ 1);
     __syncthreads();
   }
