@@ -189,6 +189,28 @@ def device_info():
     return {"error": "no GPU agent in rocminfo"}
 
 
+def vendor_gemm(dev, warmup=3, reps=20):
+    """Yardstick only: the vendor library's bf16 GEMM (torch.matmul, plain
+    bf16 output, no epilogue) on the block's prefill shapes, M = 8192 tokens
+    against [N, K] weights stored K-contiguous as the block stores them.  No
+    step of the block runs through it."""
+    for n, k, name in ((28672, 4096, "gate/up"), (6144, 4096, "QKV"), (4096, 4096, "o"), (4096, 14336, "down")):
+        a = torch.randn(8192, k, device=dev, dtype=torch.bfloat16)
+        w = torch.randn(n, k, device=dev, dtype=torch.bfloat16)
+        for _ in range(warmup):
+            torch.matmul(a, w.t())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, w.t())
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        log(f"[bench] vendor GEMM {name} M=8192 N={n} K={k}: {us:.1f} us = {2 * 8192 * n * k / us / 1e6:.0f} TFLOP/s")
+        del a, w
+
+
 def copy_bandwidth(dev, reps=10):
     """A plain 1 GiB device copy (1 GiB read + 1 GiB written), timed with
     events: the measured HBM rate, reported beside the 8 TB/s specification."""
@@ -483,11 +505,14 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) five times: the "
                          "reference reading for scaling the HBM byte counters")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor library's plain bf16 GEMM (torch.matmul) on the block's "
+                         "four prefill shapes: a yardstick for the library's own GEMM kernels")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: there is no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    device = None if args.copy_calibration else device_info()
+    device = None if (args.copy_calibration or args.vendor_gemm) else device_info()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -499,6 +524,9 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: 5 x {src.numel() * 4} bytes read and written")
+        return
+    if args.vendor_gemm:
+        vendor_gemm(dev)
         return
     binding.lib()
     if device is not None:
