@@ -303,7 +303,7 @@ def bench_chunked_prefill(wl, dev, args, history=24576):
            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "attention": {"avg_us": round(at_us, 2), "flops": att,
                          "tflops": round(att / (at_us * 1e-6) / 1e12, 1) if n_at else None},
-           "kernels": kernel_table(kernels, wm.step_work(sh, B, T))}
+           "kernels": kernel_table(kernels, wm.step_work(sh, B, T, history=history))}
     del step, w, x, kc, vc, ws, y
     torch.cuda.empty_cache()
     return out

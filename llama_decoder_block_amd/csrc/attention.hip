@@ -160,7 +160,9 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
   if (tid < kFRows) {
     const int t = t0 + tid % TQ;
     int vis = -1;
-    if (t < a.Tq) vis = a.positions ? a.positions[static_cast<int64_t>(b) * a.Tq + t] : t;
+    // a position past the cache sees the whole cache (as in the decode
+    // kernels), so the tile count stays bounded by the cache length
+    if (t < a.Tq) vis = min(a.positions ? a.positions[static_cast<int64_t>(b) * a.Tq + t] : t, a.S - 1);
     vis_s[tid] = vis;
   }
   __syncthreads();

@@ -20,6 +20,7 @@
 //   K % 8 != 0.
 #include <type_traits>
 
+#include "buffer_sizes.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -270,13 +271,15 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
   const uint32_t voff = static_cast<uint32_t>(rbase) * row_bytes + static_cast<uint32_t>(chunk) * 16u;
 
   // Each 32-row group of an operand gets its own buffer resource whose base is
-  // the group's first row and whose size ends at the operand's last row, so
-  // the per-lane offset is just (row within group, chunk, K position); rows
-  // past the end read as zero.  The resources are uniform (SALU arithmetic).
+  // the group's first row and whose size ends at the group's last row (or the
+  // operand's, if that comes first), so the per-lane offset is just (row
+  // within group, chunk, K position); rows past the end read as zero.  A
+  // group never reads past its 32 rows, so the size is clamped to them: the
+  // byte count then stays below 2^32 however many rows the operand has.  The
+  // resources are uniform (SALU arithmetic).
   auto group_rsrc = [&](const bf16_t* base, int first_row, int rows) {
-    const int left = rows - first_row;
-    const uint32_t bytes = left > 0 ? static_cast<uint32_t>(left) * row_bytes : 0u;
-    const bf16_t* p = left > 0 ? base + static_cast<int64_t>(first_row) * K : base;
+    const uint32_t bytes = group_bytes(rows, first_row, row_bytes);
+    const bf16_t* p = bytes > 0 ? base + static_cast<int64_t>(first_row) * K : base;
     return make_rsrc(p, bytes);
   };
   auto w_rsrc = [&](int g) {
@@ -894,14 +897,12 @@ hipError_t launch_mfma(const bf16_t* X, const WRows<bf16_t>& W, int M, int N, in
 }
 
 
-// The buffer-load kernel needs every 32-row group of a tile inside one weight
-// segment and byte offsets that fit in 32 bits.
-bool rs_ok(const WSeg& w, int N, bool dual) {
+// The buffer-load kernels need every 32-row group of a tile inside one weight
+// segment and a group's byte size and offsets inside 32 bits (K bounded).
+bool rs_ok(const WSeg& w, int K) {
   for (int i = 1; i < w.nseg; ++i)
-    if (w.start[i] % 32 != 0) return false;
-  (void)dual;
-  (void)N;
-  return true;
+    if (w.start[i] % kGroupRows != 0) return false;
+  return K <= kMaxGroupK;
 }
 
 BufOperands buf_operands(const bf16_t* x, const WSeg& w, int N, bool dual) {
@@ -988,7 +989,7 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
 
   const bf16_t* xp = static_cast<const bf16_t*>(X);
   auto rows = make_rows<bf16_t>(W, K);
-  if (skinny_shape(dt, M, K) && rs_ok(W, N, dual)) {
+  if (skinny_shape(dt, M, K) && rs_ok(W, K)) {
     const int n_logical = dual ? 2 * N : N;
     const int splits = skinny_splits(n_logical, K);
     const int ks = K / splits;
@@ -1034,7 +1035,7 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
   }
   if (p.splits <= 1) {
     if (kernel_name) *kernel_name = dual ? "gemm_mfma_gate_up_silu" : "gemm_mfma";
-    if (p.big && rs_ok(W, N, dual)) {
+    if (p.big && rs_ok(W, K)) {
       const int tiles_m = ceil_div(M, 256);
       const int tiles_n = ceil_div(N, dual ? 128 : 256);
       dim3 grid(tiles_m * tiles_n);

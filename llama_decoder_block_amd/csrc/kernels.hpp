@@ -108,7 +108,9 @@ struct EpiResid {
 // Q/K/V projection epilogue: RoPE on the Q and K columns (adjacent pairs
 // (2k, 2k+1) of each head rotated by pos * theta^(-2k/hd)), then the stores:
 // Q to q[m, :]; K and V either to k/v[m, :] (no cache) or to the caches at
-// slot positions[m] of sequence m / seq_len.
+// slot positions[m] of sequence m / seq_len.  A token whose position lies
+// outside [0, kv_cap) has no cache slot: its K and V are not stored (its Q
+// still is), as the 8-bit and paged cache writers skip such rows.
 template <typename T>
 struct EpiQkv {
   T* q;
@@ -120,6 +122,10 @@ struct EpiQkv {
                     // or null: angles evaluated here from `rope` (few rows)
   RopeTable rope;
 
+  // a K/V store of a cached token with no slot in [0, kv_cap)
+  __device__ __forceinline__ bool no_slot(int n, int pos) const {
+    return n >= nq_hd && kv_cap > 0 && (pos < 0 || pos >= kv_cap);
+  }
   __device__ __forceinline__ T* dest(int m, int n, int pos) const {
     if (n < nq_hd) return q + static_cast<int64_t>(m) * nq_hd + n;
     const bool is_k = n < nq_hd + nkv_hd;
@@ -163,6 +169,7 @@ struct EpiQkv {
     return f32x4{c0, s0, c1, s1};
   }
   __device__ __forceinline__ void put(const Row& r, int n, f32x4 t, const float a[4]) const {
+    if (no_slot(n, r.pos)) return;
     float o[4] = {a[0], a[1], a[2], a[3]};
     T* d;
     if (n < nq_hd) {
@@ -182,6 +189,7 @@ struct EpiQkv {
   }
   __device__ __forceinline__ void operator()(int m, int n, const float v4[4], int cnt) const {
     const int pos = kv_cap > 0 ? positions[m] : 0;
+    if (no_slot(n, pos)) return;
     float v[4] = {v4[0], v4[1], v4[2], v4[3]};
     const bool rot = n < nq_hd + nkv_hd;  // Q or K: rotate the pairs; V is stored as is
     if (cnt == 4 && (hd & 3) == 0) {
@@ -205,8 +213,9 @@ struct EpiQkv {
       return;
     }
     for (int pr = 0; pr + 1 < cnt; pr += 2) {
+      if (no_slot(n + pr, pos)) continue;  // the group may start in Q and end in K
       float a = v[pr], b = v[pr + 1];
-      if (rot) {
+      if (n + pr < nq_hd + nkv_hd) {  // per pair: the group may also straddle K and V
         f32x2 t;
         if (cs)
           t = *reinterpret_cast<const f32x2*>(angle(m, n + pr));

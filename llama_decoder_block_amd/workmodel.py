@@ -105,14 +105,16 @@ def gemm_flops(m, n, k):
     return 2 * m * n * k
 
 
-def step_work(s, batch, seq, attend_len=None, wbytes=2, rbytes=4, kv_bytes=None):
+def step_work(s, batch, seq, attend_len=None, wbytes=2, rbytes=4, kv_bytes=None, history=0):
     """Algorithmic FLOPs and HBM bytes of each step of one block forward.
 
     Returns {step: (flops, bytes)} keyed like the library's timing records
     (attn_norm, qkv_rope, attention, o_resid, ffn_norm, gate_up_silu,
     down_resid).  `attend_len` is None for a prefill without a cache (causal
     pairs within the sequence) and the number of visible cache slots for a
-    one-token decode.  Bytes: every weight, input and output read or written
+    one-token decode.  `history` (prefill only) is the number of cached slots
+    before a chunk of `seq` tokens: each token also sees them, and they are
+    read once.  Bytes: every weight, input and output read or written
     once; for decode attention only the K/V slots are counted (the query and
     output are 1/4000 of it).  `wbytes` / `rbytes` are the element sizes of
     the GEMM operands and of the residual stream; kv_bytes=FP8KV_BYTES_PER_ELEM
@@ -127,7 +129,8 @@ def step_work(s, batch, seq, attend_len=None, wbytes=2, rbytes=4, kv_bytes=None)
     out["attn_norm"] = (0, norm_bytes)
     out["qkv_rope"] = (gemm_flops(m, nqkv, d), (nqkv * d + m * d + m * nqkv) * wbytes)
     if attend_len is None:
-        out["attention"] = (prefill_attention_flops(s, batch, seq), m * (nqkv + nqo) * wbytes)
+        out["attention"] = (chunk_attention_flops(s, batch, seq, history),
+                            (m * (nqkv + nqo) + batch * history * 2 * s.n_kv * hd) * wbytes)
     else:
         kvb = (decode_attention_bytes_fp8kv(s, batch, attend_len) if kv_bytes == FP8KV_BYTES_PER_ELEM
                else decode_attention_bytes(s, batch, attend_len, wbytes))

@@ -96,3 +96,39 @@ def test_lm_head_empty():
     torch.cuda.synchronize()
     assert rc == 0
     assert unchanged(token) and unchanged(logits) and unchanged(best)
+
+
+@pytest.mark.parametrize("seq", [1, 256])
+def test_cache_positions_outside_the_cache_are_not_stored(seq):
+    """A token whose position lies outside [0, kv_cap) has no cache slot: the
+    block forward stores no K or V for it (those cache rows keep a sentinel)
+    and still writes every in-range token's slot.  seq = 1: a decode step of
+    four sequences at positions kv_cap, -1, 17 and kv_cap - 1 (K/V stored by
+    the split-K reduction's epilogue); seq = 256: a prefill into a cache, one
+    sequence at 0..255 and one at -56..159 then kv_cap..kv_cap+39 (the staged
+    GEMM epilogue)."""
+    cap = 300
+    if seq == 1:
+        pos = torch.tensor([[cap], [-1], [17], [cap - 1]], dtype=torch.int32)
+    else:
+        r = torch.arange(seq, dtype=torch.int32)
+        second = r - 56
+        second[-40:] = torch.arange(cap, cap + 40, dtype=torch.int32)
+        pos = torch.stack([r, second])
+    B = pos.shape[0]
+    wl = synth.workload("llama3_8b_gqa_prefill", batch=B, seq=seq, d_model=512, n_q=8, n_kv=2, head_dim=128,
+                        d_ff=1024)
+    inp = synth.make_block_inputs(wl)
+    w = {n: t.to(DEV) for n, t in inp.weights.items()}
+    kc = filled((B, cap, wl.n_kv, wl.head_dim), torch.bfloat16)
+    vc = filled((B, cap, wl.n_kv, wl.head_dim), torch.bfloat16)
+    binding.block_forward(inp.x.to(DEV), w, pos.to(DEV), wl.n_q, wl.n_kv, wl.theta, wl.eps, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    written = torch.zeros(B, cap, dtype=torch.bool)
+    for b in range(B):
+        for p in pos[b].tolist():
+            if 0 <= p < cap:
+                written[b, p] = True
+    for c in (kc, vc):
+        sentinel_rows = (c.cpu() == SENTINEL).all(dim=-1).all(dim=-1)
+        assert torch.equal(sentinel_rows, ~written)

@@ -73,3 +73,17 @@ def test_chunk_attention_flops():
     assert wm.chunk_attention_flops(s, 64, 1, 4096) == wm.decode_attention_flops(s, 64, 4097)
     assert (wm.chunk_attention_flops(s, 1, 3000, 0) + wm.chunk_attention_flops(s, 1, 5192, 3000)
             == wm.prefill_attention_flops(s, 1, 8192))
+
+
+def test_step_work_of_a_chunk_counts_the_cached_history():
+    """The attention row of a chunk after `history` cached slots carries the
+    chunk's own count (each token sees the history plus the causal part of
+    the chunk) and reads the history's K and V once."""
+    s = wm.Shape(4096, 32, 8, 128, 14336)
+    plain = wm.step_work(s, 1, 8192)
+    chunk = wm.step_work(s, 1, 8192, history=24576)
+    assert plain["attention"][0] == wm.prefill_attention_flops(s, 1, 8192)
+    assert chunk["attention"][0] == wm.chunk_attention_flops(s, 1, 8192, 24576)
+    assert chunk["attention"][1] - plain["attention"][1] == 24576 * wm.kv_bytes_per_token(s)
+    for k in ("qkv_rope", "o_resid", "gate_up_silu", "down_resid"):
+        assert chunk[k] == plain[k]
