@@ -107,15 +107,16 @@ def softmax_last(s):
 # ----------------------------------------------------------------------------
 def bf16_prefill_weights(s):
     """Storage-point model of the prefill path's softmax weights, for scaled
-    scores ``s`` [..., S] (-inf where masked): with z = s * log2(e) and the
-    integer offset M = ceil(max z) per row, the weights exp2(z - M) enter the
-    weighted sum of V rounded RNE to bf16, while the denominator sums them
-    unrounded.  Multiplying a weight by a power of two commutes with the
-    rounding, so any integer offset gives the same normalised result.
+    scores ``s`` [..., S] (-inf where masked).  The softmax of [L3] §4.5
+    subtracts the row maximum, exponentiates and normalises; the bf16 path
+    keeps the unnormalised weights p_j = exp(s_j - max s) as a bf16 tensor for
+    the weighted sum of V (A19: P is one of the tensors it stores in bf16), so
+    here each p_j is rounded RNE to bf16 while the normalising sum adds the
+    unrounded p_j.  The weight of the maximum is exactly 1.
     Returns (rounded weights, denominator [..., 1])."""
-    z = _as64(s) * np.log2(np.e)
-    m = np.ceil(np.max(z, axis=-1, keepdims=True))
-    e = np.exp2(z - m)
+    s = _as64(s)
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
     return round_bf16(e), np.sum(e, axis=-1, keepdims=True)
 
 

@@ -466,29 +466,39 @@ def attend_one(scores, v, bf16_weights):
 
 
 def test_prefill_weights_hand_example():
-    """Scores 0.3 and -0.2 in log2 units: offset ceil(0.3) = 1, weights 2^-0.7
-    and 2^-1.2 round to the bf16 values 0.6171875 (158/256) and 0.435546875
-    (223/512); the denominator keeps the unrounded sum."""
+    """Scores 0.3 ln 2 and -0.2 ln 2: the row maximum is the first, so the
+    unnormalised weights are exp(0) = 1 and exp(-0.5 ln 2) = 2^-0.5; rounded
+    to bf16 they are 1 and 0.70703125 (181/256), while the denominator keeps
+    the unrounded sum 1 + 2^-0.5."""
     ln2 = math.log(2.0)
     out = attend_one([0.3 * ln2, -0.2 * ln2], [[1.0, 0.0], [0.0, 1.0]], True)
-    den = 2.0 ** -0.7 + 2.0 ** -1.2
-    np.testing.assert_allclose(out, [0.6171875 / den, 0.435546875 / den], rtol=1e-14)
-    # an offset without the ceiling (0.3) would give weights 1 and bf16(2^-0.5)
-    assert abs(out[0] - 1.0 / (1.0 + 2.0 ** -0.5)) > 1e-3
+    den = 1.0 + 2.0 ** -0.5
+    np.testing.assert_allclose(out, [1.0 / den, 0.70703125 / den], rtol=1e-14)
+    # an integer offset ceil(max) instead of the maximum itself would round
+    # 2^-0.7 and 2^-1.2 (to 158/256 and 223/512) and give other outputs
+    den_c = 2.0 ** -0.7 + 2.0 ** -1.2
+    assert abs(out[0] - 0.6171875 / den_c) > 1e-3
+    assert abs(out[1] - 0.435546875 / den_c) > 2e-4
 
 
 def test_prefill_weights_uniform_scores_give_mean():
-    """Equal scores c: every weight is e = 2^(z - ceil z), z = c log2(e),
-    rounded to the same bf16 value, over a denominator of 7e, so the output
-    is mean(v) scaled by bf16(e) / e (exactly the mean when z is an integer)."""
+    """Equal scores c: every weight is exp(c - c) = 1, exact in bf16, over a
+    denominator of 7, so the output is exactly mean(v) whatever c is."""
     g = rng(28)
     v = g.standard_normal((7, 4))
-    for c in (0.0, 2.5, -13.0):
-        z = c * math.log2(math.e)
-        e = 2.0 ** (z - math.ceil(z))
-        r = oracle.round_bf16(e) / e
-        np.testing.assert_allclose(attend_one([c] * 7, v, True), v.mean(axis=0) * r, rtol=1e-13, atol=1e-15)
-    np.testing.assert_allclose(attend_one([0.0] * 7, v, True), v.mean(axis=0), rtol=1e-13, atol=1e-15)
+    for c in (0.0, 2.5, -13.0, 0.3):
+        np.testing.assert_allclose(attend_one([c] * 7, v, True), v.mean(axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_prefill_weights_maximum_counts_exactly_once():
+    """The maximum's weight is 1 whatever its score: a row of one score s0
+    and others at least 500 below it (weights exp(-500) and less, which round
+    to zero in bf16 and vanish from the fp64 denominator) gives exactly v at
+    the maximum's slot."""
+    v = rng(32).standard_normal((5, 3))
+    for s0 in (7.25, -3.5, 0.0):
+        scores = [s0 - 500.0, s0 - 600.0, s0, s0 - 700.0, s0 - 800.0]
+        np.testing.assert_array_equal(attend_one(scores, v, True), v[2])
 
 
 def test_prefill_weights_representable_equal_exact():
