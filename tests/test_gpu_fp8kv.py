@@ -16,7 +16,8 @@ import torch
 import oracle
 from oracle import fp8
 from llama_decoder_block_amd import binding, synth
-from metrics import BF16_ULP, max_abs, rel_frobenius, report, to64
+from attn_bound import check_attention
+from metrics import max_abs, rel_frobenius, report, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -42,11 +43,6 @@ def rows_with_spread(seed, shape, dtype):
 def upload_cache(kc, vc, ks, vs):
     """Dense row-major device copies (the layouts the library reads)."""
     return tuple(dev(torch.from_numpy(np.ascontiguousarray(a))) for a in (kc, vc, ks, vs))
-
-
-def attention_bound(ref, v):
-    vmax = np.abs(v).max()
-    return BF16_ULP * (np.abs(ref) + vmax) + 1e-5
 
 
 @pytest.mark.parametrize("hd", [64, 128, 256])
@@ -144,9 +140,7 @@ def test_decode_attention_fp8kv(nq, nkv):
     out, used = kernel_used(lambda: binding.gqa_attention_fp8kv(dev(q), gk8, gv8, gks, gvs,
                                                                 dev(torch.from_numpy(pos.astype(np.int32)))))
     assert used == ["attention/attn_decode_wg_fp8kv"]
-    ref = oracle.gqa_attention(to64(q), kd, vd, pos[:, None])
-    report(f"decode fp8kv {nq}/{nkv}", out, ref)
-    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, vd))
+    check_attention(f"decode fp8kv {nq}/{nkv}", out, q, kd, vd, pos[:, None], bf16_weights=False)
 
 
 def test_decode_attention_fp8kv_long_context_split():
@@ -162,9 +156,7 @@ def test_decode_attention_fp8kv_long_context_split():
     out, used = kernel_used(lambda: binding.gqa_attention_fp8kv(dev(q), gk8, gv8, gks, gvs,
                                                                 dev(torch.from_numpy(pos.astype(np.int32)))))
     assert used == ["attention/attn_decode_splitk_fp8kv"]
-    ref = oracle.gqa_attention(to64(q), kd, vd, pos[:, None])
-    report("decode fp8kv split", out, ref)
-    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, vd))
+    check_attention("decode fp8kv split", out, q, kd, vd, pos[:, None], bf16_weights=False)
 
 
 @pytest.mark.parametrize("cfg", [dict(d_model=512, n_q=8, n_kv=2, d_ff=1376, kv_cap=67),

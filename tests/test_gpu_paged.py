@@ -12,10 +12,10 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 from oracle import paged
 from llama_decoder_block_amd import binding, synth
-from metrics import BF16_ULP, report, to64
+from attn_bound import check_attention
+from metrics import report, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -23,11 +23,6 @@ DEV = "cuda"
 
 def dev(t):
     return t.to(DEV)
-
-
-def attention_bound(ref, v):
-    vmax = np.abs(v).max()
-    return BF16_ULP * (np.abs(ref) + vmax) + 1e-5
 
 
 def kernel_used(fn):
@@ -99,9 +94,7 @@ def test_decode_attention_paged(nq, nkv, P):
     out, used = kernel_used(lambda: binding.gqa_attention_paged(
         dev(q), dev(kpool), dev(vpool), dev(torch.from_numpy(table)), dev(torch.from_numpy(pos.astype(np.int32)))))
     assert used == ["attention/attn_decode_wg_paged"]
-    ref = oracle.gqa_attention(to64(q), kc, vc, pos[:, None])
-    report(f"decode paged {nq}/{nkv} P{P}", out, ref)
-    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, vc))
+    check_attention(f"decode paged {nq}/{nkv} P{P}", out, q, kc, vc, pos[:, None], bf16_weights=False)
 
 
 def test_decode_attention_paged_long_context_split():
@@ -122,6 +115,4 @@ def test_decode_attention_paged_long_context_split():
     out, used = kernel_used(lambda: binding.gqa_attention_paged(
         dev(q), dev(kpool), dev(vpool), dev(torch.from_numpy(table)), dev(torch.from_numpy(pos.astype(np.int32)))))
     assert used == ["attention/attn_decode_splitk_paged"]
-    ref = oracle.gqa_attention(to64(q), kc, vc, pos[:, None])
-    report("decode paged split", out, ref)
-    assert np.all(np.abs(to64(out) - ref) <= attention_bound(ref, vc))
+    check_attention("decode paged split", out, q, kc, vc, pos[:, None], bf16_weights=False)
