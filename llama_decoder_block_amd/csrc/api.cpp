@@ -453,7 +453,7 @@ int run_block(const void* x, void* y, const llama_block_weights* w, const int32_
     // epilogue evaluates them itself and the extra launch is skipped.
     const bool table = M > kRopeInlineRows;
     ep.rope_cs = table ? rope_cs : nullptr;
-    ep.rope = &rope;
+    ep.rope_base = std::pow(rope_theta, -2.0 / static_cast<double>(hd));
     e = timed("qkv_rope", s, [&](const char** name) {
       if (table) {
         hipError_t er = lb::launch_rope_table(positions, M, hd, rope, wdt, rope_cs, s);

@@ -38,7 +38,6 @@ namespace lb {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescale = 8.0f;  // lazy-rescale threshold of the flash kernel (log2 units)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -297,15 +296,16 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[h2][e]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
-    // Lazy rescaling: the reference maximum m_run only moves when a row's
-    // tile maximum exceeds it by more than kRescale (log2 units), so most
-    // tiles skip rescaling O and l.  Any reference gives the same softmax;
-    // the weights stay <= 2^kRescale.  The reference is kept an integer, so
-    // rescaling multiplies by an exact power of two and each weight's bf16
-    // rounding is that of exp2(score * c - M) for any integer M: the same
-    // whatever the tile order.
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescale) != 0) {
-      const float m_new = ceilf(fmaxf(m_run, tmax));
+    // Online softmax: whenever the tile raises some row's maximum, every row
+    // of the wavefront moves its reference m_run to its running maximum
+    // (rows whose maximum did not move rescale by exactly 1).  The weights
+    // exp2(score * c - m_run) are rounded to bf16 for the PV product, so a
+    // reference equal to the row maximum keeps the largest weight exactly 1
+    // and free of rounding error, as in the softmax that subtracts the row
+    // maximum; only weights of tiles seen before the maximum are rounded
+    // against an earlier reference.
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;

@@ -15,13 +15,16 @@ constexpr int kGroupRows = 32;
 // per-lane offsets below 2^32: 32 rows x K x 2 bytes < 2^32.
 constexpr int64_t kMaxGroupK = (int64_t{1} << 26) - 1;
 
-// Bytes a group starting at `first_row` of an operand with `rows` rows of
-// `row_bytes` bytes may read: at most its own 32 rows, none past the
-// operand's last row, zero when the group starts past the end.
-constexpr uint32_t group_bytes(int64_t rows, int64_t first_row, uint32_t row_bytes) {
-  const int64_t left = rows - first_row;
-  const int64_t n = left < kGroupRows ? left : kGroupRows;
-  return n > 0 ? static_cast<uint32_t>(n) * row_bytes : 0u;
+// Bytes a group starting at `first_row` (>= 0) of an operand with `rows`
+// rows of `row_bytes` bytes may read: at most its own 32 rows, none past the
+// operand's last row, zero when the group starts past the end.  32-bit
+// arithmetic on purpose: in a kernel the operands are wave-uniform and must
+// stay on the scalar unit (a 64-bit comparison would move them to vector
+// registers and every buffer load that uses the size into a read-first-lane
+// loop).
+constexpr uint32_t group_bytes(int32_t rows, int32_t first_row, uint32_t row_bytes) {
+  const int32_t left = rows - first_row;
+  return left > 0 ? static_cast<uint32_t>(left < kGroupRows ? left : kGroupRows) * row_bytes : 0u;
 }
 
 }  // namespace lb

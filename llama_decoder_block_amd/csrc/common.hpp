@@ -115,6 +115,20 @@ struct RopeTable {
   double inv_freq[128];  // k = 0 .. hd/2-1 (hd <= 256)
 };
 
+// theta_base^(-2k/hd) as base^k with base = theta_base^(-2/hd), by binary
+// powering in fp64 (k < 128: at most 7 squarings; relative error about
+// k * 2^-53, so at any int32 position the angle moves by < 1e-9 rad).  Used
+// where a per-pair table would have to travel by value with the kernel.
+__device__ __forceinline__ double rope_inv_freq_pow(double base, int k) {
+  double r = 1.0, b = base;
+  while (k) {
+    if (k & 1) r *= b;
+    b *= b;
+    k >>= 1;
+  }
+  return r;
+}
+
 // Angle reduction in fp64: phi = pos * inv_freq is formed and reduced to
 // [-1/2, 1/2] revolutions exactly enough (~1e-16 relative) for any int32
 // position; the reduced angle then has an fp32 error of ~2e-7 rad.

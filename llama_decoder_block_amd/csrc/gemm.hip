@@ -28,6 +28,15 @@ namespace lb {
 
 namespace {
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // weight row resolution over up to three segments
 // ---------------------------------------------------------------------------
@@ -228,6 +237,132 @@ gemm_mfma_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, in
 }
 
 // ---------------------------------------------------------------------------
+// Epilogue of the 256 x 256 tile kernels (4 wavefronts in a 2 x 2 grid, each
+// holding 4 x 4 accumulator tiles of 32 x 32): register e of a 32x32 tile is
+// feature row (e/4)*8 + half*4 + e%4 of the weight operand and token column
+// lane%32.  `lds` is the K loop's LDS, free once every wavefront has passed
+// the barrier at the top of the staged path.
+// ---------------------------------------------------------------------------
+template <bool DUAL, class Epi>
+__device__ __forceinline__ void tile_epilogue(const f32x16 (&acc)[4][4], u32x4* lds, int m0, int out_n0, int M,
+                                              int N, const Epi& epi) {
+  constexpr int BN = 256, BM = 256, WN = 128, WM = 128, TN = 4, TM = 4;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wave_n = wid & 1, wave_m = wid >> 1;
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  if constexpr (!DUAL) {
+    // Whole tile inside the output: the staged epilogue.  The K loop's LDS
+    // buffers are free now; each wavefront passes its 128 x 128 block through
+    // its own LDS region one 32-token block at a time, so that afterwards a
+    // lane holds four consecutive columns of one token and each store (and
+    // each load of pre(), e.g. the residual or the rotation table) covers
+    // whole rows: 32 lanes x 16 bytes of one token, instead of 32 tokens x
+    // 16 bytes.  The next block's pre() loads are issued before the current
+    // block is stored.  Per-token keys (positions) are loaded once for all
+    // four blocks and shared between lanes.
+    if (m0 + BM <= M && out_n0 + BN <= N && epi.vec_ok()) {
+      constexpr int SROW = WN + 4;  // floats per staged token row (16 lanes of a read hit 64 distinct banks)
+      __syncthreads();              // every wavefront is done with the K loop's fragments
+      // lane values derived from a copy made here, so that nothing of the
+      // epilogue is computed before the K loop and kept live through it
+      int le = lane;
+      asm volatile("" : "+v"(le));
+      float* stage = reinterpret_cast<float*>(lds) + wid * (32 * SROW);
+      const int g = le & 31, hsel = le >> 5, srow = le & 31, shalf = le >> 5;
+      const int n = out_n0 + wave_n * WN + g * 4;
+      const int mw = m0 + wave_m * WM;
+      int key[TM];
+#pragma unroll
+      for (int b = 0; b < TM; ++b) key[b] = Epi::kRowKey ? epi.row_key(mw + b * 32 + g) : 0;
+      // row of token 2i + hsel of block b (iteration i: lanes 0-31 one token, 32-63 the next)
+      auto row_of = [&](int b, int i) {
+        const int t = 2 * i + hsel;
+        return epi.row_from(mw + b * 32 + t, Epi::kRowKey ? __shfl(key[b], t, 64) : 0);
+      };
+      // chunks of CH iterations (16 / CH per block); chunk c + 1's pre()
+      // loads are issued before chunk c is stored.  CH is the largest that
+      // leaves the K loop free of register spills for each epilogue.
+      constexpr int CH = Epi::kRowKey ? 8 : 4, NCH = 16 / CH;
+      f32x4 pre[2][CH];
+      auto issue = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) pre[c & 1][i] = epi.pre(row_of(c / NCH, (c % NCH) * CH + i), n);
+      };
+      issue(0);
+      // chunk c's accumulator tile acc[.][c / NCH] must be a compile-time
+      // index (a runtime one puts all of acc in scratch memory), so the loop
+      // is unrolled by template recursion rather than left to the unroller
+      static_for<0, NCH * TM>([&](auto C) {
+        constexpr int c = decltype(C)::value;
+        constexpr int b = c / NCH, i0 = (c % NCH) * CH;
+        if constexpr (i0 == 0) {
+          // register e of tile (a, b): token frag_row, column a*32 + (e/4)*8 + frag_half*4 + e%4
+#pragma unroll
+          for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              f32x4 t = f32x4{acc[a][b][4 * j], acc[a][b][4 * j + 1], acc[a][b][4 * j + 2], acc[a][b][4 * j + 3]};
+              asm volatile("" : "+v"(t));  // through VGPRs (left to itself the allocator spills in the K loop)
+              *reinterpret_cast<f32x4*>(stage + srow * SROW + a * 32 + j * 8 + shalf * 4) = t;
+            }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        f32x4 val[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+          val[i] = *reinterpret_cast<const f32x4*>(stage + (2 * (i0 + i) + hsel) * SROW + g * 4);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next block overwrites it
+        if constexpr (c + 1 < NCH * TM) issue(c + 1);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const float v[4] = {val[i][0], val[i][1], val[i][2], val[i][3]};
+          epi.put(row_of(b, i0 + i), n, pre[c & 1][i], v);
+        }
+      });
+      return;
+    }
+  }
+  // per-fragment path (partial tiles, the fused gate/up product): the tile
+  // indices a, b must be compile-time (a runtime index puts all of acc in
+  // scratch memory), so the loops are unrolled by template recursion
+  static_for<0, TM>([&](auto B) {
+    constexpr int b = decltype(B)::value;
+    const int m = m0 + wave_m * WM + b * 32 + frag_row;
+    if (m >= M) return;
+    if constexpr (DUAL) {
+      static_for<0, TN / 2>([&](auto A) {
+        constexpr int a = decltype(A)::value;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = out_n0 + wave_n * (WN / 2) + a * 32 + j * 8 + frag_half * 4;
+          if (c >= N) continue;
+          float g[4], u[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            g[i] = acc[a][b][j * 4 + i];
+            u[i] = acc[a + TN / 2][b][j * 4 + i];
+          }
+          epi(m, c, g, u, min(4, N - c));
+        }
+      });
+    } else {
+      static_for<0, TN>([&](auto A) {
+        constexpr int a = decltype(A)::value;
+        static_for<0, 4>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          const int n = out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4;
+          if (n >= N) return;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
+          epi(m, n, v, min(4, N - n));
+        });
+      });
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
 // MFMA kernel, large tiles, register-staged buffer loads ("rs" kernel).
 // 256 x 256 output tile, four wavefronts (one per SIMD) in a 2 x 2 grid, each
 // owning 128 x 128 as 4 x 4 tiles of 32 x 32 (accumulators in AGPRs).
@@ -279,7 +414,7 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
   // resources are uniform (SALU arithmetic).
   auto group_rsrc = [&](const bf16_t* base, int first_row, int rows) {
     const uint32_t bytes = group_bytes(rows, first_row, row_bytes);
-    const bf16_t* p = bytes > 0 ? base + static_cast<int64_t>(first_row) * K : base;
+    const bf16_t* p = rows > first_row ? base + static_cast<int64_t>(first_row) * K : base;
     return make_rsrc(p, bytes);
   };
   auto w_rsrc = [&](int g) {
@@ -427,110 +562,7 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
   }
   if (kt < KT) kstep(kt, I0{}, I1{}, I0{});
 
-  // epilogue: register e of a 32x32 tile is feature row (e/4)*8 + half*4 + e%4
-  // of the weight operand and token column lane%32
-  if constexpr (!DUAL) {
-    // Whole tile inside the output: the staged epilogue.  The K loop's LDS
-    // buffers are free now; each wavefront passes its 128 x 128 block through
-    // its own LDS region one 32-token block at a time, so that afterwards a
-    // lane holds four consecutive columns of one token and each store (and
-    // each load of pre(), e.g. the residual or the rotation table) covers
-    // whole rows: 32 lanes x 16 bytes of one token, instead of 32 tokens x
-    // 16 bytes.  The next block's pre() loads are issued before the current
-    // block is stored.  Per-token keys (positions) are loaded once for all
-    // four blocks and shared between lanes.
-    if (m0 + BM <= M && out_n0 + BN <= N && epi.vec_ok()) {
-      constexpr int SROW = WN + 4;  // floats per staged token row (16 lanes of a read hit 64 distinct banks)
-      __syncthreads();              // every wavefront is done with the K loop's fragments
-      // lane values derived from a copy made here, so that nothing of the
-      // epilogue is computed before the K loop and kept live through it
-      int le = lane;
-      asm volatile("" : "+v"(le));
-      float* stage = reinterpret_cast<float*>(&lds[0][0]) + wid * (32 * SROW);
-      const int g = le & 31, hsel = le >> 5, srow = le & 31, shalf = le >> 5;
-      const int n = out_n0 + wave_n * WN + g * 4;
-      const int mw = m0 + wave_m * WM;
-      int key[TM];
-#pragma unroll
-      for (int b = 0; b < TM; ++b) key[b] = Epi::kRowKey ? epi.row_key(mw + b * 32 + g) : 0;
-      // row of token 2i + hsel of block b (iteration i: lanes 0-31 one token, 32-63 the next)
-      auto row_of = [&](int b, int i) {
-        const int t = 2 * i + hsel;
-        return epi.row_from(mw + b * 32 + t, Epi::kRowKey ? __shfl(key[b], t, 64) : 0);
-      };
-      // chunks of CH iterations (16 / CH per block); chunk c + 1's pre()
-      // loads are issued before chunk c is stored.  CH is the largest that
-      // leaves the K loop free of register spills for each epilogue.
-      constexpr int CH = Epi::kRowKey ? 8 : 4, NCH = 16 / CH;
-      f32x4 pre[2][CH];
-      auto issue = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) pre[c & 1][i] = epi.pre(row_of(c / NCH, (c % NCH) * CH + i), n);
-      };
-      issue(0);
-#pragma unroll
-      for (int c = 0; c < NCH * TM; ++c) {
-        const int b = c / NCH, i0 = (c % NCH) * CH;
-        if (i0 == 0) {
-          // register e of tile (a, b): token frag_row, column a*32 + (e/4)*8 + frag_half*4 + e%4
-#pragma unroll
-          for (int a = 0; a < TN; ++a)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              f32x4 t = f32x4{acc[a][b][4 * j], acc[a][b][4 * j + 1], acc[a][b][4 * j + 2], acc[a][b][4 * j + 3]};
-              asm volatile("" : "+v"(t));  // through VGPRs (left to itself the allocator spills in the K loop)
-              *reinterpret_cast<f32x4*>(stage + srow * SROW + a * 32 + j * 8 + shalf * 4) = t;
-            }
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        }
-        f32x4 val[CH];
-#pragma unroll
-        for (int i = 0; i < CH; ++i)
-          val[i] = *reinterpret_cast<const f32x4*>(stage + (2 * (i0 + i) + hsel) * SROW + g * 4);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next block overwrites it
-        if (c + 1 < NCH * TM) issue(c + 1);
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-          const float v[4] = {val[i][0], val[i][1], val[i][2], val[i][3]};
-          epi.put(row_of(b, i0 + i), n, pre[c & 1][i], v);
-        }
-      }
-      return;
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < TM; ++b) {
-    const int m = m0 + wave_m * WM + b * 32 + frag_row;
-    if (m >= M) continue;
-    if constexpr (DUAL) {
-#pragma unroll
-      for (int a = 0; a < TN / 2; ++a)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = out_n0 + wave_n * (WN / 2) + a * 32 + j * 8 + frag_half * 4;
-          if (c >= N) continue;
-          float g[4], u[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            g[i] = acc[a][b][j * 4 + i];
-            u[i] = acc[a + TN / 2][b][j * 4 + i];
-          }
-          epi(m, c, g, u, min(4, N - c));
-        }
-    } else {
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = out_n0 + wave_n * WN + a * 32 + j * 8 + frag_half * 4;
-          if (n >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[a][b][j * 4 + i];
-          epi(m, n, v, min(4, N - n));
-        }
-    }
-  }
+  tile_epilogue<DUAL>(acc, &lds[0][0], m0, out_n0, M, N, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -870,10 +902,10 @@ hipError_t with_epi(const GemmEpi& e, F&& f) {
       if (e.out_dt == DType::F32)
         return f(EpiQkv<float>{static_cast<float*>(e.q), static_cast<float*>(e.k),
                                static_cast<float*>(e.v), e.positions, e.nq_hd, e.nkv_hd, e.hd,
-                               e.seq_len, e.kv_cap, e.rope_cs, *e.rope});
+                               e.seq_len, e.kv_cap, e.rope_cs, e.rope_base});
       return f(EpiQkv<bf16_t>{static_cast<bf16_t*>(e.q), static_cast<bf16_t*>(e.k),
                               static_cast<bf16_t*>(e.v), e.positions, e.nq_hd, e.nkv_hd, e.hd,
-                              e.seq_len, e.kv_cap, e.rope_cs, *e.rope});
+                              e.seq_len, e.kv_cap, e.rope_cs, e.rope_base});
     default:
       return hipErrorInvalidValue;
   }

@@ -119,8 +119,8 @@ struct EpiQkv {
   const int32_t* positions;
   int nq_hd, nkv_hd, hd, seq_len, kv_cap;
   const float* cs;  // [M, hd/2] (cos, sin) of each row's rotation angles (launch_rope_table),
-                    // or null: angles evaluated here from `rope` (few rows)
-  RopeTable rope;
+                    // or null: angles evaluated here (few rows) with theta_k = rope_base^k
+  double rope_base;  // theta_base^(-2/hd)
 
   // a K/V store of a cached token with no slot in [0, kv_cap)
   __device__ __forceinline__ bool no_slot(int n, int pos) const {
@@ -164,8 +164,8 @@ struct EpiQkv {
     if (cs) return *reinterpret_cast<const f32x4*>(angle(static_cast<int>(r.m), n));
     const int k = (n % hd) >> 1;
     float s0, c0, s1, c1;
-    rope_sincos_t<T>(r.pos, rope.inv_freq[k], &s0, &c0);
-    rope_sincos_t<T>(r.pos, rope.inv_freq[k + 1], &s1, &c1);
+    rope_sincos_t<T>(r.pos, rope_inv_freq_pow(rope_base, k), &s0, &c0);
+    rope_sincos_t<T>(r.pos, rope_inv_freq_pow(rope_base, k + 1), &s1, &c1);
     return f32x4{c0, s0, c1, s1};
   }
   __device__ __forceinline__ void put(const Row& r, int n, f32x4 t, const float a[4]) const {
@@ -201,8 +201,8 @@ struct EpiQkv {
         } else {
           const int k = (n % hd) >> 1;
           float s0, c0, s1, c1;
-          rope_sincos_t<T>(positions[m], rope.inv_freq[k], &s0, &c0);
-          rope_sincos_t<T>(positions[m], rope.inv_freq[k + 1], &s1, &c1);
+          rope_sincos_t<T>(positions[m], rope_inv_freq_pow(rope_base, k), &s0, &c0);
+          rope_sincos_t<T>(positions[m], rope_inv_freq_pow(rope_base, k + 1), &s1, &c1);
           t = f32x4{c0, s0, c1, s1};
         }
         const float a0 = v[0] * t[0] - v[1] * t[1], b0 = v[0] * t[1] + v[1] * t[0];
@@ -213,24 +213,26 @@ struct EpiQkv {
       return;
     }
     for (int pr = 0; pr + 1 < cnt; pr += 2) {
-      if (no_slot(n + pr, pos)) continue;  // the group may start in Q and end in K
       float a = v[pr], b = v[pr + 1];
-      if (n + pr < nq_hd + nkv_hd) {  // per pair: the group may also straddle K and V
+      // per pair: a group of four columns may straddle Q and K or K and V
+      if (n + pr < nq_hd + nkv_hd) {
         f32x2 t;
         if (cs)
           t = *reinterpret_cast<const f32x2*>(angle(m, n + pr));
         else {
           float s0, c0;
-          rope_sincos_t<T>(positions[m], rope.inv_freq[((n + pr) % hd) >> 1], &s0, &c0);
+          rope_sincos_t<T>(positions[m], rope_inv_freq_pow(rope_base, ((n + pr) % hd) >> 1), &s0, &c0);
           t = f32x2{c0, s0};
         }
         const float ra = a * t[0] - b * t[1];
         b = a * t[1] + b * t[0];
         a = ra;
       }
-      T* d = dest(m, n + pr, pos);
-      st(d, a);
-      st(d + 1, b);
+      if (!no_slot(n + pr, pos)) {
+        T* d = dest(m, n + pr, pos);
+        st(d, a);
+        st(d + 1, b);
+      }
     }
   }
 };
@@ -286,7 +288,7 @@ struct GemmEpi {
   const int32_t* positions;
   int nq_hd, nkv_hd, hd, seq_len, kv_cap;
   const float* rope_cs;  // [M, hd/2] (cos, sin) table from launch_rope_table, or null
-  const RopeTable* rope;  // the inverse frequencies (used when rope_cs is null)
+  double rope_base;       // theta_base^(-2/hd) (angles evaluated in the epilogue when rope_cs is null)
 };
 
 // Workspace bytes the GEMM needs for a given problem (split-K partials).

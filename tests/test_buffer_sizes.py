@@ -19,7 +19,8 @@ PROGRAM = r"""
 #include "buffer_sizes.hpp"
 int main(int argc, char** argv) {
   for (int i = 1; i + 2 < argc; i += 3) {
-    const long long rows = atoll(argv[i]), first = atoll(argv[i + 1]), k = atoll(argv[i + 2]);
+    const int rows = atoi(argv[i]), first = atoi(argv[i + 1]);
+    const long long k = atoll(argv[i + 2]);
     const unsigned row_bytes = static_cast<unsigned>(k * 2);
     std::printf("%u\n", lb::group_bytes(rows, first, row_bytes));
   }
