@@ -48,8 +48,14 @@ def check(h, gamma, w, eps, tag):
     return t
 
 
-@pytest.mark.parametrize("n,d,vocab", [(64, 4096, 32000), (37, 4096, 32000), (5, 512, 1001), (300, 256, 4000)])
+@pytest.mark.parametrize("n,d,vocab", [(64, 4096, 128256), (64, 4096, 32000), (37, 4096, 32000), (5, 512, 1001),
+                                        (300, 256, 4000)])
 def test_lm_head_argmax(n, d, vocab):
+    """64 x 4096 -> 128256 is the head of "LLaMA-3 8B 现代 LLM 架构、计算规模与能耗"
+    §十 for the 64 sequences of the decode workload (the argmax over 31 full
+    4096-column chunks and a partial last one of 1280); the other shapes cover ragged row counts,
+    a vocabulary that is not a multiple of the chunk, and more rows than one
+    skinny GEMM takes."""
     h = synth.normal(400, (n, d))
     gamma = synth.normal(401, (d,), 0.01, 1.0, dtype="bf16")
     w = synth.normal(402, (vocab, d), 0.02, dtype="bf16")
