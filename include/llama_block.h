@@ -166,6 +166,28 @@ size_t llama_block_forward_workspace_bytes(int32_t batch, int32_t seq_len, int32
                                            int32_t head_dim, int32_t d_ff, int32_t kv_cap,
                                            int wdtype, int rdtype);
 
+/* llama_block_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same operation, arguments and kernels, minus the
+ * workspace.  Its scratch is a fixed device array of
+ * LLAMA_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held from
+ * the first call on that GPU until the process ends; the call makes no
+ * allocation of any kind (with the library's opt-in profiler off).
+ * A call whose workspace (llama_block_forward_workspace_bytes of the same
+ * shape) exceeds LLAMA_NOALLOC_SCRATCH_BYTES returns
+ * LLAMA_ERR_WORKSPACE_TOO_SMALL before enqueueing anything.  Every call on a
+ * GPU shares that GPU's scratch: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialized by the caller.
+ * The stream must belong to the current device (LLAMA_ERR_INVALID_ARGUMENT
+ * otherwise).  At 64 MiB the scratch holds, for example, the Llama-3-8B
+ * decode step of 64 sequences or a prefill of several hundred tokens. */
+#define LLAMA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int llama_block_forward_noalloc(const void* x, void* y, const llama_block_weights* w,
+                                const int32_t* positions, void* k_cache, void* v_cache, int32_t kv_cap,
+                                int32_t batch, int32_t seq_len, int32_t d_model, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t head_dim, int32_t d_ff, double rope_theta,
+                                double eps, int wdtype, int rdtype, void* stream);
+
 /* 8-bit KV cache ([LA] "Troubleshooting Common Deployment Faults", item 3:
  * an 8-bit KV cache halves the bytes_per_elem factor of the KV-cache memory
  * formula in [LA] §4).  The pages fix no format or scale; this library uses

@@ -26,7 +26,10 @@ FUNCTIONS = [
     "llama_gqa_attention_fp8kv_workspace_bytes", "llama_block_forward_fp8kv",
     "llama_block_forward_fp8kv_workspace_bytes", "llama_kv_append_paged", "llama_gqa_attention_paged",
     "llama_gqa_attention_paged_workspace_bytes", "llama_lm_head_argmax", "llama_lm_head_argmax_workspace_bytes",
+    "llama_block_forward_noalloc",
 ]
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LLAMA_NOALLOC_SCRATCH_BYTES
 
 
 class LlamaError(RuntimeError):
@@ -94,6 +97,8 @@ def lib():
         "llama_lm_head_argmax": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _f64, _int, _int, _vp, _sz, _vp],
                                  _int),
         "llama_lm_head_argmax_workspace_bytes": ([_i64, _i32, _i32, _int, _int], _sz),
+        "llama_block_forward_noalloc": ([_vp, _vp, ctypes.POINTER(BlockWeights), _vp, _vp, _vp, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _i32, _i32, _f64, _f64, _int, _int, _vp], _int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -216,6 +221,22 @@ def block_forward(x, w, positions, n_q_heads, n_kv_heads, rope_theta, eps, k_cac
     _check(L.llama_block_forward(_p(x), _p(y), ctypes.byref(wt), _p(positions), _p(k_cache), _p(v_cache),
                                  kv_cap, B, T, d, n_q_heads, n_kv_heads, hd, dff, rope_theta, eps, wdt, rdt,
                                  _p(ws), nbytes, _stream()))
+    return y
+
+
+def block_forward_noalloc(x, w, positions, n_q_heads, n_kv_heads, rope_theta, eps, k_cache=None, v_cache=None,
+                          y=None):
+    """block_forward on the library's fixed device scratch (no workspace)."""
+    B, T, d = x.shape
+    hd = w["wq"].shape[0] // n_q_heads
+    dff = w["w_gate"].shape[0]
+    kv_cap = k_cache.shape[1] if k_cache is not None else 0
+    if y is None:
+        y = torch.empty_like(x)
+    wt = make_weights(w)
+    _check(lib().llama_block_forward_noalloc(_p(x), _p(y), ctypes.byref(wt), _p(positions), _p(k_cache),
+                                             _p(v_cache), kv_cap, B, T, d, n_q_heads, n_kv_heads, hd, dff,
+                                             rope_theta, eps, _dt(w["wq"]), _dt(x), _stream()))
     return y
 
 

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -517,12 +518,14 @@ int run_block(const void* x, void* y, const llama_block_weights* w, const int32_
 
 }  // namespace
 
-int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
-                        const int32_t* positions, void* k_cache, void* v_cache, int32_t kv_cap,
-                        int32_t batch, int32_t seq_len, int32_t d_model, int32_t n_q_heads,
-                        int32_t n_kv_heads, int32_t head_dim, int32_t d_ff, double rope_theta,
-                        double eps, int wdtype, int rdtype, void* workspace, size_t ws_bytes,
-                        void* stream) {
+namespace {
+
+// Validation of llama_block_forward and llama_block_forward_noalloc (all but
+// the workspace): LLAMA_OK to go on, or the status to return.
+int check_block_call(const void* x, void* y, const llama_block_weights* w, const int32_t* positions,
+                     void* k_cache, void* v_cache, int32_t kv_cap, int32_t batch, int32_t seq_len,
+                     int32_t d_model, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t d_ff,
+                     double rope_theta, double eps, int wdtype, int rdtype) {
   if (!dtype_ok(wdtype) || !dtype_ok(rdtype))
     return fail(LLAMA_ERR_UNSUPPORTED, "unknown dtype code (wdtype=%d rdtype=%d)", wdtype, rdtype);
   int st = check_block_args(x, y, w, positions, batch, seq_len, d_model, n_q_heads, n_kv_heads, head_dim, d_ff,
@@ -531,13 +534,107 @@ int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
   const bool has_cache = kv_cap > 0;
   if (has_cache != (k_cache != nullptr) || has_cache != (v_cache != nullptr))
     return fail(LLAMA_ERR_INVALID_ARGUMENT, "k_cache and v_cache must both be given exactly when kv_cap > 0");
-  if (batch == 0 || seq_len == 0) return ok();
-  for (const void* p : std::initializer_list<const void*>{static_cast<const void*>(k_cache),
-                                                          static_cast<const void*>(v_cache), workspace})
+  return LLAMA_OK;
+}
+
+// Alignment of the caches and the workspace (checked once the call is known
+// to do work, as for every entry point).
+int check_block_buffers(const void* k_cache, const void* v_cache, const void* workspace) {
+  for (const void* p : std::initializer_list<const void*>{k_cache, v_cache, workspace})
     if (p && !aligned16(p)) return fail(LLAMA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+int llama_block_forward(const void* x, void* y, const llama_block_weights* w,
+                        const int32_t* positions, void* k_cache, void* v_cache, int32_t kv_cap,
+                        int32_t batch, int32_t seq_len, int32_t d_model, int32_t n_q_heads,
+                        int32_t n_kv_heads, int32_t head_dim, int32_t d_ff, double rope_theta,
+                        double eps, int wdtype, int rdtype, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  int st = check_block_call(x, y, w, positions, k_cache, v_cache, kv_cap, batch, seq_len, d_model, n_q_heads,
+                            n_kv_heads, head_dim, d_ff, rope_theta, eps, wdtype, rdtype);
+  if (st != LLAMA_OK) return st;
+  if (batch == 0 || seq_len == 0) return ok();
+  st = check_block_buffers(k_cache, v_cache, workspace);
+  if (st != LLAMA_OK) return st;
   return run_block(x, y, w, positions, k_cache, v_cache, kv_cap, batch, seq_len, d_model, n_q_heads, n_kv_heads,
                    head_dim, d_ff, rope_theta, eps, static_cast<DType>(wdtype), static_cast<DType>(rdtype),
                    workspace, ws_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// llama_block_forward_noalloc: the block forward on a fixed device scratch
+// ---------------------------------------------------------------------------
+namespace {
+
+// The scratch of llama_block_forward_noalloc (what llama_block_forward takes
+// as its workspace): a fixed array in the library's code object.  Every GPU
+// the library runs on holds its own copy, at its own address, until the
+// process ends.  In host code the array's name is not a device address: the
+// address of each GPU's copy comes from hipGetSymbolAddress, looked up once
+// per device with that device current and kept in g_scratch_ptr.
+__device__ __align__(256) uint8_t scratch[LLAMA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` and the device's index.
+hipError_t current_scratch(void** ptr, int* dev) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return e;
+  if (*dev < 0 || *dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[*dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[*dev] = p;
+  }
+  *ptr = g_scratch_ptr[*dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+int llama_block_forward_noalloc(const void* x, void* y, const llama_block_weights* w,
+                                const int32_t* positions, void* k_cache, void* v_cache, int32_t kv_cap,
+                                int32_t batch, int32_t seq_len, int32_t d_model, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t head_dim, int32_t d_ff, double rope_theta,
+                                double eps, int wdtype, int rdtype, void* stream) {
+  int st = check_block_call(x, y, w, positions, k_cache, v_cache, kv_cap, batch, seq_len, d_model, n_q_heads,
+                            n_kv_heads, head_dim, d_ff, rope_theta, eps, wdtype, rdtype);
+  if (st != LLAMA_OK) return st;
+  if (batch == 0 || seq_len == 0) return ok();
+  st = check_block_buffers(k_cache, v_cache, nullptr);
+  if (st != LLAMA_OK) return st;
+  const size_t need = block_plan(batch, seq_len, d_model, n_q_heads, n_kv_heads, head_dim, d_ff, kv_cap,
+                                 static_cast<DType>(wdtype), static_cast<DType>(rdtype))
+                          .total;
+  if (need > LLAMA_NOALLOC_SCRATCH_BYTES)
+    return fail(LLAMA_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of scratch; the fixed scratch holds %zu "
+                "(llama_block_forward with a caller workspace takes any size)",
+                need, static_cast<size_t>(LLAMA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  int dev = -1;
+  hipError_t e = current_scratch(&ws, &dev);
+  if (e != hipSuccess) return hip_fail(e, "llama_block_forward_noalloc: scratch address");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (s) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "llama_block_forward_noalloc: stream device");
+    if (sdev != dev)
+      return fail(LLAMA_ERR_INVALID_ARGUMENT, "the stream belongs to device %d but device %d is current",
+                  static_cast<int>(sdev), dev);
+  }
+  return run_block(x, y, w, positions, k_cache, v_cache, kv_cap, batch, seq_len, d_model, n_q_heads, n_kv_heads,
+                   head_dim, d_ff, rope_theta, eps, static_cast<DType>(wdtype), static_cast<DType>(rdtype), ws,
+                   LLAMA_NOALLOC_SCRATCH_BYTES, s, nullptr);
 }
 
 // ---------------------------------------------------------------------------

@@ -152,6 +152,36 @@ def test_block_validation():
     assert L.llama_block_forward_workspace_bytes(0, 16, 256, 4, 2, 64, 512, 0, 1, 0) == 0
 
 
+def block_noalloc(L, **kw):
+    w = binding.BlockWeights(*([FAKE + 0x1000 * i for i in range(1, 10)]))
+    a = dict(x=FAKE, y=FAKE + 0x100, w=ctypes.byref(w), pos=FAKE + 0x200, kc=None, vc=None, cap=0, B=1, T=16,
+             d=256, nq=4, nkv=2, hd=64, dff=512, theta=1e4, eps=1e-5, wdt=1, rdt=0)
+    a.update(kw)
+    return L.llama_block_forward_noalloc(a["x"], a["y"], a["w"], a["pos"], a["kc"], a["vc"], a["cap"], a["B"],
+                                         a["T"], a["d"], a["nq"], a["nkv"], a["hd"], a["dff"], a["theta"], a["eps"],
+                                         a["wdt"], a["rdt"], None)
+
+
+def test_block_noalloc_validation_and_scratch_limit():
+    """The entry point without a workspace validates like llama_block_forward
+    and rejects, before touching the GPU, any call whose workspace would
+    exceed the fixed scratch (LLAMA_NOALLOC_SCRATCH_BYTES)."""
+    L = binding.lib()
+    assert block_noalloc(L, nkv=3) == -1
+    assert block_noalloc(L, cap=64) == -1
+    assert block_noalloc(L, y=FAKE) == -1
+    assert block_noalloc(L, hd=300) == -2
+    assert block_noalloc(L, B=0) == 0
+    # the Llama-3-8B prefill of 8192 tokens needs ~0.6 GB: refused
+    big = L.llama_block_forward_workspace_bytes(1, 8192, 4096, 32, 8, 128, 14336, 0, 1, 0)
+    assert big > binding.NOALLOC_SCRATCH_BYTES
+    assert block_noalloc(L, T=8192, d=4096, nq=32, nkv=8, hd=128, dff=14336) == -3
+    assert b"fixed scratch" in L.llama_last_error()
+    # the 64-sequence decode step at 4097 slots fits
+    dec = L.llama_block_forward_workspace_bytes(64, 1, 4096, 32, 8, 128, 14336, 4097, 1, 0)
+    assert 0 < dec <= binding.NOALLOC_SCRATCH_BYTES
+
+
 def test_empty_calls_are_noops():
     L = binding.lib()
     assert block(L, B=0) == 0
