@@ -8,9 +8,11 @@
 // fp32 accumulation; the weight tile is the MFMA "A" operand and the
 // activations the "B" operand, so each lane holds four consecutive output
 // features of one token: RoPE pairs and 4-wide stores stay inside a lane):
-// gemm_mfma_rs_kernel: prefill (M >= 512, K % 64 == 0, weight segments on
-//   32-row boundaries).  256x256 tiles, one wavefront per SIMD owning 128x128,
-//   register-staged buffer loads two K steps ahead, XOR-swizzled LDS.
+// gemm_mfma_dma_kernel / gemm_mfma_rs_kernel: prefill (M >= 512, K % 64 == 0,
+//   weight segments on 32-row boundaries).  256x256 tiles, one wavefront per
+//   SIMD owning 128x128, XOR-swizzled LDS; operands loaded straight into LDS
+//   one K step ahead (dma, K <= 8192) or through registers two steps ahead
+//   (rs, longer K).
 // gemm_skinny_kernel: decode (M <= 64, K % 256 == 0): streams the weights once
 //   with whole-line loads, K split over the wavefronts and summed in LDS.
 // gemm_mfma_kernel: generic tiles (64x64 .. 256x256) for every other bf16
@@ -84,6 +86,8 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int 
 // MFMA kernel
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;
+// longest K (elements) the LDS-DMA prefill kernel takes (see launch_gemm)
+constexpr int kDmaMaxK = 8192;
 
 
 // LDS tile rows are 128 B (64 bf16 of K).  gfx950 serves a 16-byte-per-lane
@@ -562,6 +566,171 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
   }
   if (kt < KT) kstep(kt, I0{}, I1{}, I0{});
 
+  tile_epilogue<DUAL>(acc, &lds[0][0], m0, out_n0, M, N, epi);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel, large tiles, operands loaded straight into LDS ("dma" kernel).
+// Tile, wavefront grid, LDS layout (XOR-swizzled 128-byte rows), fragment
+// reads and epilogues are those of gemm_mfma_rs_kernel; the K loop differs.
+// Each operand row is fetched with buffer_load_dwordx4 ... lds, which writes a
+// wavefront's 64 x 16 bytes to 1 KB of LDS at M0 + 16 * lane without passing
+// through VGPRs: the wavefronts issue no LDS stores and hold no staging
+// registers.  Lane i of a load covers row i / 8 of an 8-row piece and LDS
+// chunk i % 8, so it fetches the row's logical K chunk (i % 8) ^ swizzle
+// (whole 128-byte lines per 8 lanes, as before).  Two 64 KB LDS buffers:
+// while the MFMAs consume step kt from one, the 16 loads per wavefront of
+// step kt+1 fill the other (issued between the first 32 MFMAs); every
+// wavefront's loads of step kt+1 have landed at the barrier that ends step kt.
+// Requires K % 64 == 0 and weight-segment boundaries at multiples of 32 rows.
+// ---------------------------------------------------------------------------
+template <bool DUAL, class Epi>
+__global__ void __launch_bounds__(256, 1)
+gemm_mfma_dma_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_n, Epi epi) {
+  constexpr int BN = 256, WN = 128, WM = 128, TN = 4, TM = 4;
+  __shared__ u32x4 lds[2][(BN + 256) * 8];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, &tm, &tn);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_n = wid & 1, wave_m = wid >> 1;
+  const int out_n0 = tn * (DUAL ? BN / 2 : BN);
+  const int m0 = tm * 256;
+  const int KT = K / kBK;
+  const uint32_t row_bytes = static_cast<uint32_t>(K) * 2u;
+
+  // buffer resource of a 32-row group: based at its first row, sized to its
+  // rows (rows past the operand's end read as zero); uniform (SALU)
+  auto group_rsrc = [&](const bf16_t* base, int first_row, int rows) {
+    const uint32_t bytes = group_bytes(rows, first_row, row_bytes);
+    const bf16_t* p = rows > first_row ? base + static_cast<int64_t>(first_row) * K : base;
+    return make_rsrc(p, bytes);
+  };
+  auto w_rsrc = [&](int g) {
+    if constexpr (DUAL) {
+      const int r0 = 32 * g, wv = r0 / WN, rr0 = r0 % WN;
+      const int c0 = out_n0 + wv * (WN / 2) + (rr0 % (WN / 2));
+      return group_rsrc(rr0 >= WN / 2 ? op.w[1] : op.w[0], c0, N);
+    } else {
+      const int n0 = out_n0 + 32 * g;
+      if (n0 < op.s1) return group_rsrc(op.w[0], n0, op.wrows[0]);
+      if (n0 < op.s2) return group_rsrc(op.w[1], n0 - op.s1, op.wrows[1]);
+      return group_rsrc(op.w[2], n0 - op.s2, op.wrows[2]);
+    }
+  };
+  // this wavefront's groups: weight groups 2 wid, 2 wid + 1 and token groups
+  // 2 wid, 2 wid + 1 (of 8 each), each as four pieces of 8 rows
+  const __amdgpu_buffer_rsrc_t rs[4] = {w_rsrc(2 * wid), w_rsrc(2 * wid + 1),
+                                        group_rsrc(op.x, m0 + 64 * wid, M),
+                                        group_rsrc(op.x, m0 + 64 * wid + 32, M)};
+  // row r = 32 g + 8 q + lane / 8 holds logical chunk c at LDS chunk
+  // c ^ ((r >> 1) & 7) = c ^ (4 (q & 1) + lane / 16): lane i fetches logical
+  // chunk (i % 8) ^ that
+  const int r8 = lane >> 3, pc = lane & 7;
+  const uint32_t voff0 = static_cast<uint32_t>(r8) * row_bytes + static_cast<uint32_t>(pc ^ (r8 >> 1)) * 16u;
+  const uint32_t voff1 = static_cast<uint32_t>(r8) * row_bytes + static_cast<uint32_t>(pc ^ (4 + (r8 >> 1))) * 16u;
+  // piece p = 0..15 of step kt into buffer BUF: operand p / 8, group p / 4 % 2, quarter p % 4
+  auto dma = [&](auto BUFc, int kt, int p) {
+    constexpr int buf = decltype(BUFc)::value;
+    const int opnd = p >> 3, gi = (p >> 2) & 1, q = p & 3;
+    const int row = 32 * (2 * wid + gi) + 8 * q;
+    u32x4* dst = &lds[buf][(opnd ? BN * 8 : 0) + row * 8];
+    const uint32_t soff = static_cast<uint32_t>(kt) * (kBK * 2) + static_cast<uint32_t>(8 * q) * row_bytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[opnd * 2 + gi], (__attribute__((address_space(3))) void*)dst, 16,
+                                             (q & 1) ? voff1 : voff0, soff, 0, 0);
+  };
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  bf16x8 fa[2][TN], fb[2][TM];
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto rd = [&](auto BUFc, int sub, auto F, int i) {
+    constexpr int buf = decltype(BUFc)::value, f = decltype(F)::value;
+    const int ch = sub * 2 + frag_half;
+    if (i < TN)
+      fa[f][i] = __builtin_bit_cast(bf16x8, lds[buf][lds_idx(wave_n * WN + i * 32 + frag_row, ch)]);
+    else
+      fb[f][i - TN] = __builtin_bit_cast(bf16x8, lds[buf][BN * 8 + lds_idx(wave_m * WM + (i - TN) * 32 + frag_row, ch)]);
+  };
+  auto mf = [&](auto F, int t) {
+    constexpr int f = decltype(F)::value;
+    acc[t / TM][t % TM] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][t / TM], fb[f][t % TM], acc[t / TM][t % TM], 0, 0, 0);
+    fence();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // One K step on buffer CUR (fragments of sub-step 0 already read into set
+  // 0): sub-steps 0 and 1 issue the next step's 16 loads into the other
+  // buffer between their first 8 MFMAs, sub-steps 0..2 read the next
+  // sub-step's fragments between MFMAs 8..15, and sub-step 3 waits for the
+  // loads, crosses the barrier half-way and reads the next step's first
+  // fragments between its last MFMAs.  Straight-line: the last step's loads
+  // of a step past the end are issued too (they read in-bounds bytes of the
+  // next row, or zeros past a group's last row, into the idle buffer, and
+  // have landed at the step's final barrier, before the epilogue reuses LDS);
+  // its fragment reads past the end are never used.
+  auto kstep = [&](int kt, auto CUR) {
+    constexpr int cur = decltype(CUR)::value;
+    using NXT = std::integral_constant<int, 1 - cur>;
+    auto sub = [&](auto F, auto NF, int s) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        mf(F, t);
+        if (s < 2) {
+          dma(NXT{}, kt + 1, 8 * s + t);
+          fence();
+        }
+      }
+#pragma unroll
+      for (int t = 8; t < 16; ++t) {
+        mf(F, t);
+        rd(CUR, s + 1, NF, t - 8);
+        fence();
+      }
+    };
+    sub(I0{}, I1{}, 0);
+    sub(I1{}, I0{}, 1);
+    sub(I0{}, I1{}, 2);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) mf(I1{}, t);
+    fence();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rd(NXT{}, 0, I0{}, 2 * i);
+      rd(NXT{}, 0, I0{}, 2 * i + 1);
+      fence();
+      mf(I1{}, 8 + i);
+    }
+#pragma unroll
+    for (int t = 12; t < 16; ++t) mf(I1{}, t);
+  };
+
+  // prologue: step 0 into buffer 0
+#pragma unroll
+  for (int p = 0; p < 16; ++p) dma(I0{}, 0, p);
+  fence();
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  fence();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rd(I0{}, 0, I0{}, i);
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    kstep(kt, I0{});
+    kstep(kt + 1, I1{});
+  }
+  if (kt < KT) kstep(kt, I0{});
   tile_epilogue<DUAL>(acc, &lds[0][0], m0, out_n0, M, N, epi);
 }
 
@@ -1072,16 +1241,24 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
       const int tiles_n = ceil_div(N, dual ? 128 : 256);
       dim3 grid(tiles_m * tiles_n);
       BufOperands op = buf_operands(xp, W, N, dual);
+      // Operands straight into LDS for K up to kDmaMaxK; past it the
+      // register-staged kernel, whose loads run two K steps ahead instead of
+      // one (measured on MI355X: gate/up 1475 against 1519 us, QKV 398
+      // against 412, o equal, but down at K = 14336 863 against 762 us, with
+      // more L2 misses left exposed and a busier texture addresser)
+      const bool dma = K <= kDmaMaxK;
+      auto go = [&](auto kern, auto e) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, op, M, N, K, tiles_m, tiles_n, e);
+        return hipGetLastError();
+      };
       if (dual)
         return with_silu(epi, [&](auto e) {
-          hipLaunchKernelGGL((gemm_mfma_rs_kernel<true, decltype(e)>), grid, dim3(256), 0, s, op, M, N, K,
-                             tiles_m, tiles_n, e);
-          return hipGetLastError();
+          using E = decltype(e);
+          return dma ? go(gemm_mfma_dma_kernel<true, E>, e) : go(gemm_mfma_rs_kernel<true, E>, e);
         });
       return with_epi(epi, [&](auto e) {
-        hipLaunchKernelGGL((gemm_mfma_rs_kernel<false, decltype(e)>), grid, dim3(256), 0, s, op, M, N, K,
-                           tiles_m, tiles_n, e);
-        return hipGetLastError();
+        using E = decltype(e);
+        return dma ? go(gemm_mfma_dma_kernel<false, E>, e) : go(gemm_mfma_rs_kernel<false, E>, e);
       });
     }
     if (p.bn == 256 && p.bm == 256) {
