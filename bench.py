@@ -14,7 +14,11 @@ value      = prefill block-forward TFLOP/s (algorithmic FLOPs: linear layers
 roofline   = the dominant kernel (fused gate/up GEMM + SiLU product):
              algorithmic FLOPs per launch / its average launch time, measured
              with HIP events recorded on the kernel's stream inside the timed
-             region
+             region; traffic = its HBM bytes per launch from two rocprofv3
+             counter passes (FETCH_SIZE, WRITE_SIZE) run by this script on the
+             same kernel, calibrated by a plain 1 GiB copy in the same passes
+mha_prefill = the Llama-7B and Llama-65B MHA prefill workloads, timed like
+             the headline prefill, against their 60%-of-peak target times
 kernels    = every timed step of the path: launches, average time, and the
              achieved TFLOP/s (GEMMs, attention) or GB/s (norms)
 decode     = the decode step (1 GiB read between steps so that weights and
@@ -51,24 +55,7 @@ PREFILL = "llama3_8b_gqa_prefill"
 DECODE = "llama3_8b_gqa_decode"
 DOMINANT = "gate_up_silu/gemm_mfma_gate_up_silu"
 DECODE_ATTN = "attention/attn_decode_wg"
-# HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE passes (KiB per dispatch), each scaled by the same counter's
-# reading for a plain device copy of known size (bench.py --copy-calibration:
-# FETCH_SIZE reads half the bytes the copy reads, WRITE_SIZE all of them).
-# Valid only for the GEMM sources it was measured on: reported as null once
-# their hash changes.
-TRAFFIC = {"bytes": 3116004512, "fetch_scale": 2.0, "write_scale": 1.0,
-           "sources_sha256": "d67f4dd61304640e8da918a82324396292c67a1540a52c31e706070530a338f1"}
-TRAFFIC_SOURCES = ("gemm.hip", "kernels.hpp", "common.hpp")
-
-
-def dominant_traffic():
-    import hashlib
-    h = hashlib.sha256()
-    for name in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, "llama_decoder_block_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return TRAFFIC["bytes"] if h.hexdigest() == TRAFFIC["sources_sha256"] else None
+MHA_TARGET_MS = {"llama7b_mha_prefill": 0.572, "llama65b_mha_prefill": 8.966}  # 60% of the bf16 MFMA peak
 
 
 def log(*a):
@@ -493,6 +480,151 @@ def bench_lm_head(wd, dev, args, vocab=128256):
             "kernels": rows}
 
 
+# ---------------------------------------------------------------------------
+# HBM bytes per launch from two rocprofv3 counter passes (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch), each scaled by the same counter's reading for
+# a plain copy of known size run in the same pass.  The passes run this file
+# with --traffic-pass as a child process of the profiler.
+# ---------------------------------------------------------------------------
+COPY_ELEMS = 1 << 28  # fp32: the calibration copy reads 1 GiB and writes 1 GiB
+
+
+def traffic_pass():
+    """Child of the profiler: the prefill's gate/up GEMM (with its down GEMM,
+    through the FFN entry point), the standalone RoPE on the prefill's q and
+    k, an RMSNorm of the prefill's fp32 rows and the calibration copy, each
+    launched three times on inputs drawn on the GPU."""
+    dev = "cuda:0"
+    wl = synth.workload(PREFILL)
+    M, d, dff, hd = wl.batch * wl.seq, wl.d_model, wl.d_ff, wl.head_dim
+    g = torch.Generator(device=dev).manual_seed(1000 * wl.index + 95)
+    bf = torch.bfloat16
+    f = torch.randn(M, d, generator=g, device=dev).to(bf)
+    wg = (torch.randn(dff, d, generator=g, device=dev) * 0.02).to(bf)
+    wu = (torch.randn(dff, d, generator=g, device=dev) * 0.02).to(bf)
+    wd = (torch.randn(d, dff, generator=g, device=dev) * 0.02).to(bf)
+    h = torch.randn(M, d, generator=g, device=dev)
+    y = torch.empty_like(h)
+    q = torch.randn(M, wl.n_q, hd, generator=g, device=dev).to(bf)
+    k = torch.randn(M, wl.n_kv, hd, generator=g, device=dev).to(bf)
+    pos = torch.arange(M, dtype=torch.int32, device=dev)
+    gamma = (1 + 0.01 * torch.randn(d, generator=g, device=dev)).to(bf)
+    normed = torch.empty(M, d, dtype=bf, device=dev)
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        binding.swiglu_ffn(f, wg, wu, wd, residual=h, out=y)
+        binding.rope(q, k, pos, wl.theta)
+        binding.rmsnorm(h, gamma, wl.eps, out=normed)
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print("traffic pass done", flush=True)
+
+
+def _counter_pass(counter, tmp):
+    """One profiled child run; returns {kernel class: [KiB per dispatch]}."""
+    import csv
+    rocprof = "/opt/rocm/bin/rocprofv3" if os.path.exists("/opt/rocm/bin/rocprofv3") else "rocprofv3"
+    out = os.path.join(tmp, counter)
+    env = dict(os.environ, TMPDIR="/tmp")
+    cmd = [rocprof, "--kernel-trace", "--pmc", counter, "--output-format", "csv", "-d", out, "-o", "run", "--",
+           sys.executable, os.path.abspath(__file__), "--traffic-pass"]
+    r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True, timeout=240)
+    if "traffic pass done" not in r.stdout:
+        raise RuntimeError(f"{counter} pass failed (rc {r.returncode}): {r.stderr[-400:]}")
+    per = {}
+    with open(os.path.join(out, "run_counter_collection.csv")) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            if "gemm_mfma" in name and "<true" in name:
+                cls = "gate_up"
+            elif "rope_heads" in name:
+                cls = "rope"
+            elif "rmsnorm" in name:
+                cls = "rmsnorm"
+            elif "neg" in name.lower():
+                cls = "copy"
+            else:
+                continue
+            per.setdefault(cls, {}).setdefault(row["Dispatch_Id"], 0.0)
+            per[cls][row["Dispatch_Id"]] += float(row["Counter_Value"])
+    return {c: list(v.values()) for c, v in per.items()}
+
+
+def measure_traffic(algorithmic):
+    """Calibrated HBM bytes per launch of the gate/up GEMM, the standalone RoPE
+    and the RMSNorm: (FETCH_SIZE x fetch_scale + WRITE_SIZE x write_scale) x
+    1024 with each scale = the copy's known bytes / its own counter reading.
+    `algorithmic` maps the same classes to their algorithmic bytes."""
+    import tempfile
+    tmp = tempfile.mkdtemp(prefix="traffic_", dir="/tmp")
+    fetch, write = _counter_pass("FETCH_SIZE", tmp), _counter_pass("WRITE_SIZE", tmp)
+    avg = lambda xs: sum(xs) / len(xs)
+    copy_bytes = COPY_ELEMS * 4
+    fs = copy_bytes / (avg(fetch["copy"]) * 1024)
+    ws = copy_bytes / (avg(write["copy"]) * 1024)
+    out = {"fetch_scale": round(fs, 4), "write_scale": round(ws, 4)}
+    for cls, alg in algorithmic.items():
+        fb = avg(fetch[cls]) * 1024 * fs
+        wb = avg(write[cls]) * 1024 * ws
+        out[cls] = {"bytes": int(round(fb + wb)), "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
+                    "algorithmic_bytes": int(alg), "ratio": round((fb + wb) / alg, 3)}
+    log(f"[bench] HBM traffic (counter passes): {out}")
+    return out
+
+
+def gpu_block_inputs(wl, dev):
+    """The workload's tensors drawn on the GPU (seeded torch normals with the
+    workload's distributions: x ~ N(0,1), weights N(0, 0.02^2), gains
+    1 + N(0, 0.01^2)), for timing only."""
+    g = torch.Generator(device=dev).manual_seed(1000 * wl.index + 80)
+    bf = torch.bfloat16
+    d, hd, dff, nq, nkv = wl.d_model, wl.head_dim, wl.d_ff, wl.n_q, wl.n_kv
+    shapes = {"wq": (nq * hd, d), "wk": (nkv * hd, d), "wv": (nkv * hd, d), "wo": (d, nq * hd),
+              "w_gate": (dff, d), "w_up": (dff, d), "w_down": (d, dff)}
+    w = {n: (torch.randn(sh, generator=g, device=dev) * 0.02).to(bf) for n, sh in shapes.items()}
+    for n in ("attn_norm", "ffn_norm"):
+        w[n] = (1 + 0.01 * torch.randn(d, generator=g, device=dev)).to(bf)
+    x = torch.randn(wl.batch, wl.seq, d, generator=g, device=dev).to(bf).float()
+    pos = torch.arange(wl.seq, dtype=torch.int32, device=dev).repeat(wl.batch, 1)
+    return x, w, pos
+
+
+def bench_mha_prefill(name, dev, args):
+    """A full-size MHA prefill workload (Llama-7B: B=1 T=2048 d=4096 32 heads
+    d_ff=11008; Llama-65B: B=4 T=2048 d=8192 64 heads d_ff=22016), timed like
+    the headline prefill, against the 60%-of-peak target time."""
+    wl = synth.workload(name)
+    x, w, pos = gpu_block_inputs(wl, dev)
+    need = binding.block_workspace_bytes(wl.batch, wl.seq, wl.d_model, wl.n_q, wl.n_kv, wl.head_dim, wl.d_ff, 0,
+                                         binding.BF16, binding.F32)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+
+    def step():
+        binding.block_forward(x, w, pos, wl.n_q, wl.n_kv, wl.theta, wl.eps, y=y, workspace=ws)
+    ms, per, kernels = time_steps(step, args.steps, args.warmup)
+    sh = shape_of(wl)
+    flops = wm.prefill_flops(sh, wl.batch, wl.seq)
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {name}: {ms:.3f} ms/step, {tf:.1f} TFLOP/s ({tf / MFMA_BF16_PEAK_TFLOPS:.1%} of peak; "
+        f"target {MHA_TARGET_MS[name]} ms)")
+    table = kernel_table(kernels, wm.step_work(sh, wl.batch, wl.seq))
+    for k, row in table.items():
+        log(f"[bench]   {k:40s} {row}")
+    out = {"workload": f"{name}: B={wl.batch} T={wl.seq} d={wl.d_model} n_q={wl.n_q} n_kv={wl.n_kv} "
+                       f"hd={wl.head_dim} d_ff={wl.d_ff} theta={wl.theta:g}, weights drawn on the GPU",
+           "ms_per_step": round(ms, 4), "ms_median": round(per[len(per) // 2], 4), "flops": flops,
+           "tflops": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+           "tokens_per_s": round(wl.batch * wl.seq / (ms * 1e-3), 1),
+           "target_ms": MHA_TARGET_MS[name], "kernels": table}
+    del step, x, w, pos, ws, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -505,6 +637,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) five times: the "
                          "reference reading for scaling the HBM byte counters")
+    ap.add_argument("--no-traffic", action="store_true",
+                    help="skip the two rocprofv3 counter passes that measure HBM bytes")
+    ap.add_argument("--traffic-pass", action="store_true",
+                    help="(run by the counter passes) launch the kernels whose HBM bytes are measured, then exit")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only time the vendor library's plain bf16 GEMM (torch.matmul) on the block's "
                          "four prefill shapes: a yardstick for the library's own GEMM kernels")
@@ -512,6 +648,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: there is no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_pass:
+        traffic_pass()
+        return
     device = None if (args.copy_calibration or args.vendor_gemm) else device_info()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -557,6 +696,7 @@ def main():
     torch.cuda.empty_cache()
     rope = bench_rope(wl, dev, args)
     chunked = bench_chunked_prefill(wl, dev, args)
+    mha = {n: bench_mha_prefill(n, dev, args) for n in MHA_TARGET_MS}
 
     # ---------------- decode -----------------
     decode = None
@@ -615,6 +755,19 @@ def main():
         decode["lm_head"] = bench_lm_head(wd, dev, args)
         decode["long_context"] = bench_long_decode(wd, dev, args)
 
+    traffic = None
+    if not args.no_traffic:
+        T_ = wl.batch * wl.seq
+        alg = {"gate_up": work["gate_up_silu"][1],
+               "rope": rope["bytes"],
+               "rmsnorm": T_ * wl.d_model * (4 + 2) + wl.d_model * 2}
+        try:
+            traffic = measure_traffic(alg)
+        except Exception as e:  # the profiler is an instrument, not part of the path
+            log(f"[bench] HBM traffic passes unavailable: {e}")
+            traffic = {"error": str(e)[:300]}
+        if "gate_up" in traffic:
+            rope["traffic"] = traffic["rope"]
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")
@@ -643,11 +796,17 @@ def main():
         "prefill_mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"kernel": DOMINANT, "bound": "mfma", "achieved": round(dom_tflops, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": dominant_traffic(),
+                     "frac": round(dom_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic["gate_up"]["bytes"] if traffic and "gate_up" in traffic else None,
+                     "traffic_detail": traffic.get("gate_up") if traffic else None,
                      "flops_per_launch": dom_flops, "avg_us": round(dom_avg_ms * 1e3, 2)},
         "kernels": table,
         "rope": rope,
+        "rmsnorm_traffic": traffic.get("rmsnorm") if traffic else None,
+        "traffic_calibration": ({k: traffic[k] for k in ("fetch_scale", "write_scale")}
+                                if traffic and "fetch_scale" in traffic else None),
         "chunked_prefill": chunked,
+        "mha_prefill": mha,
         "decode": decode,
         "device": device,
         "hbm_copy": copy_bw,
