@@ -88,6 +88,10 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int 
 constexpr int kBK = 64;
 // longest K (elements) the LDS-DMA prefill kernel takes (see launch_gemm)
 constexpr int kDmaMaxK = 8192;
+// compute units of the GPU the large-tile schedule is sized for, and the
+// fewest K steps a split of the large-tile kernels keeps
+constexpr int kCUs = 256;
+constexpr int kBigSplitMinSteps = 16;
 
 
 // LDS tile rows are 128 B (64 bf16 of K).  gfx950 serves a 16-byte-per-lane
@@ -393,7 +397,7 @@ struct BufOperands {
 
 template <bool DUAL, class Epi>
 __global__ void __launch_bounds__(256, 1)
-gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_n, Epi epi) {
+gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int kps, int tiles_m, int tiles_n, Epi epi) {
   constexpr int BN = 256, BM = 256, WN = 128, WM = 128, TN = 4, TM = 4;
   constexpr int GROUPS = 8;  // row groups of 32 per operand
   __shared__ u32x4 lds[2][(BN + BM) * 8];
@@ -404,7 +408,9 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
   const int wave_n = wid & 1, wave_m = wid >> 1;
   const int out_n0 = tn * (DUAL ? BN / 2 : BN);
   const int m0 = tm * BM;
-  const int KT = K / kBK;
+  // K steps [kt0, KT) of split blockIdx.z (kps steps per split)
+  const int kt0 = blockIdx.z * kps;
+  const int KT = min(K / kBK, kt0 + kps);
   const uint32_t row_bytes = static_cast<uint32_t>(K) * 2u;
   const int chunk = tid & 7, rbase = tid >> 3;
   const uint32_t voff = static_cast<uint32_t>(rbase) * row_bytes + static_cast<uint32_t>(chunk) * 16u;
@@ -552,14 +558,14 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
 
   // prologue: step 0 in LDS buffer 0 (staging set 0), step 1 in flight (set 1)
 #pragma unroll
-  for (int g = 0; g < GROUPS; ++g) gload(0, g, I0{});
+  for (int g = 0; g < GROUPS; ++g) gload(kt0, g, I0{});
 #pragma unroll
-  for (int g = 0; g < GROUPS; ++g) gload(1, g, I1{});
+  for (int g = 0; g < GROUPS; ++g) gload(kt0 + 1, g, I1{});
 #pragma unroll
   for (int g = 0; g < GROUPS; ++g) lstore(0, g, I0{});
   barrier();
   read_frags(0, 0, I0{});
-  int kt = 0;
+  int kt = kt0;
   for (; kt + 1 < KT; kt += 2) {
     kstep(kt, I0{}, I1{}, I0{});
     kstep(kt + 1, I1{}, I0{}, I1{});
@@ -586,7 +592,7 @@ gemm_mfma_rs_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_
 // ---------------------------------------------------------------------------
 template <bool DUAL, class Epi>
 __global__ void __launch_bounds__(256, 1)
-gemm_mfma_dma_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles_n, Epi epi) {
+gemm_mfma_dma_kernel(BufOperands op, int M, int N, int K, int kps, int tiles_m, int tiles_n, Epi epi) {
   constexpr int BN = 256, WN = 128, WM = 128, TN = 4, TM = 4;
   __shared__ u32x4 lds[2][(BN + 256) * 8];
 
@@ -597,7 +603,9 @@ gemm_mfma_dma_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles
   const int wave_n = wid & 1, wave_m = wid >> 1;
   const int out_n0 = tn * (DUAL ? BN / 2 : BN);
   const int m0 = tm * 256;
-  const int KT = K / kBK;
+  // K steps [kt0, KT) of split blockIdx.z (kps steps per split)
+  const int kt0 = blockIdx.z * kps;
+  const int KT = min(K / kBK, kt0 + kps);
   const uint32_t row_bytes = static_cast<uint32_t>(K) * 2u;
 
   // buffer resource of a 32-row group: based at its first row, sized to its
@@ -719,13 +727,13 @@ gemm_mfma_dma_kernel(BufOperands op, int M, int N, int K, int tiles_m, int tiles
 
   // prologue: step 0 into buffer 0
 #pragma unroll
-  for (int p = 0; p < 16; ++p) dma(I0{}, 0, p);
+  for (int p = 0; p < 16; ++p) dma(I0{}, kt0, p);
   fence();
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   fence();
 #pragma unroll
   for (int i = 0; i < 8; ++i) rd(I0{}, 0, I0{}, i);
-  int kt = 0;
+  int kt = kt0;
   for (; kt + 1 < KT; kt += 2) {
     kstep(kt, I0{});
     kstep(kt + 1, I1{});
@@ -1042,6 +1050,18 @@ Plan make_plan(DType dt, int M, int N, int K, bool dual) {
     p.bn = 256;
     p.bm = 256;
     p.big = K % kBK == 0;
+    if (p.big) {
+      // Too few 256x256 tiles to give every CU one (e.g. 2048 tokens against
+      // 4096 features: 128 tiles): split K so the grid reaches one workgroup
+      // per CU, each split keeping at least kBigSplitMinSteps K steps; fp32
+      // partial sums, then splitk_reduce_kernel applies the epilogue.
+      const int tiles = ceil_div(M, 256) * ceil_div(N, dual ? 128 : 256);
+      const int KT = K / kBK;
+      int splits = 1;
+      while (tiles * splits * 2 <= kCUs && KT / (splits * 2) >= kBigSplitMinSteps) splits *= 2;
+      p.k_per_split = ceil_div(KT, splits) * kBK;
+      p.splits = ceil_div(K, p.k_per_split);
+    }
     return p;
   }
   // few rows (decode): 64x64 tiles; split K until there are >= 512 workgroups
@@ -1234,23 +1254,24 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
       return hipGetLastError();
     });
   }
-  if (p.splits <= 1) {
+  if (p.big && rs_ok(W, K)) {
     if (kernel_name) *kernel_name = dual ? "gemm_mfma_gate_up_silu" : "gemm_mfma";
-    if (p.big && rs_ok(W, K)) {
-      const int tiles_m = ceil_div(M, 256);
-      const int tiles_n = ceil_div(N, dual ? 128 : 256);
-      dim3 grid(tiles_m * tiles_n);
-      BufOperands op = buf_operands(xp, W, N, dual);
-      // Operands straight into LDS for K up to kDmaMaxK; past it the
-      // register-staged kernel, whose loads run two K steps ahead instead of
-      // one (measured on MI355X: gate/up 1475 against 1519 us, QKV 398
-      // against 412, o equal, but down at K = 14336 863 against 762 us, with
-      // more L2 misses left exposed and a busier texture addresser)
-      const bool dma = K <= kDmaMaxK;
-      auto go = [&](auto kern, auto e) {
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, op, M, N, K, tiles_m, tiles_n, e);
-        return hipGetLastError();
-      };
+    const int tiles_m = ceil_div(M, 256);
+    const int tiles_n = ceil_div(N, dual ? 128 : 256);
+    const int kps = p.k_per_split / kBK;
+    dim3 grid(tiles_m * tiles_n, 1, p.splits);
+    BufOperands op = buf_operands(xp, W, N, dual);
+    // Operands straight into LDS for K up to kDmaMaxK; past it the
+    // register-staged kernel, whose loads run two K steps ahead instead of
+    // one (measured on MI355X: gate/up 1475 against 1519 us, QKV 398
+    // against 412, o equal, but down at K = 14336 863 against 762 us, with
+    // more L2 misses left exposed and a busier texture addresser)
+    const bool dma = K <= kDmaMaxK;
+    auto go = [&](auto kern, auto e) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, op, M, N, K, kps, tiles_m, tiles_n, e);
+      return hipGetLastError();
+    };
+    if (p.splits == 1) {
       if (dual)
         return with_silu(epi, [&](auto e) {
           using E = decltype(e);
@@ -1261,6 +1282,33 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
         return dma ? go(gemm_mfma_dma_kernel<false, E>, e) : go(gemm_mfma_rs_kernel<false, E>, e);
       });
     }
+    // K split: fp32 partials over the logical rows (gate then up), then the reduction applies the epilogue
+    const int n_logical = dual ? 2 * N : N;
+    const size_t need = static_cast<size_t>(p.splits) * M * n_logical * sizeof(float);
+    if (ws == nullptr || ws_bytes < need) return hipErrorInvalidValue;
+    if (kernel_name) *kernel_name = dual ? "gemm_mfma_splitk_big_gate_up" : "gemm_mfma_splitk_big";
+    float* part = static_cast<float*>(ws);
+    const int64_t split_stride = static_cast<int64_t>(M) * n_logical;
+    EpiPartial pe{part, n_logical, split_stride, N};
+    hipError_t err = dual ? (dma ? go(gemm_mfma_dma_kernel<true, EpiPartial>, pe) : go(gemm_mfma_rs_kernel<true, EpiPartial>, pe))
+                          : (dma ? go(gemm_mfma_dma_kernel<false, EpiPartial>, pe) : go(gemm_mfma_rs_kernel<false, EpiPartial>, pe));
+    if (err != hipSuccess) return err;
+    const int64_t threads = static_cast<int64_t>(M) * ceil_div(N, 4);
+    const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
+    if (dual)
+      return with_silu(epi, [&](auto e) {
+        hipLaunchKernelGGL((splitk_reduce_kernel<true, decltype(e)>), dim3(blocks), dim3(256), 0, s,
+                           part, p.splits, split_stride, M, N, n_logical, e);
+        return hipGetLastError();
+      });
+    return with_epi(epi, [&](auto e) {
+      hipLaunchKernelGGL((splitk_reduce_kernel<false, decltype(e)>), dim3(blocks), dim3(256), 0, s,
+                         part, p.splits, split_stride, M, N, n_logical, e);
+      return hipGetLastError();
+    });
+  }
+  if (p.splits <= 1) {
+    if (kernel_name) *kernel_name = dual ? "gemm_mfma_gate_up_silu" : "gemm_mfma";
     if (p.bn == 256 && p.bm == 256) {
       if (dual)
         return with_silu(epi, [&](auto e) {

@@ -257,10 +257,25 @@ struct EpiSilu {
 };
 
 // Raw fp32 partial sums of one K-split: part[z][m][n]
+// (split z = blockIdx.z).  For the fused gate/up product the partial rows are
+// the logical rows: gate column c at c, up column c at half + c.
 struct EpiPartial {
   float* part;
   int ldo;
   int64_t split_stride;  // elements between consecutive splits
+  int half;              // gate/up product: offset of the up columns (= N)
+  using Row = int64_t;
+  static constexpr bool kRowKey = false;
+  __device__ __forceinline__ bool vec_ok() const { return (ldo & 3) == 0; }
+  __device__ __forceinline__ Row row(int m) const {
+    return blockIdx.z * split_stride + static_cast<int64_t>(m) * ldo;
+  }
+  __device__ __forceinline__ int row_key(int) const { return 0; }
+  __device__ __forceinline__ Row row_from(int m, int) const { return row(m); }
+  __device__ __forceinline__ f32x4 pre(Row, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ void put(Row r, int n, f32x4, const float v[4]) const {
+    Vec4<float>::store(part + r + n, v);
+  }
   __device__ __forceinline__ void operator()(int m, int n, const float v[4], int cnt) const {
     float* p = part + blockIdx.z * split_stride + static_cast<int64_t>(m) * ldo + n;
     if (cnt == 4 && (ldo & 3) == 0) {
@@ -268,6 +283,10 @@ struct EpiPartial {
     } else {
       for (int i = 0; i < cnt; ++i) p[i] = v[i];
     }
+  }
+  __device__ __forceinline__ void operator()(int m, int c, const float g[4], const float u[4], int cnt) const {
+    (*this)(m, c, g, cnt);
+    (*this)(m, half + c, u, cnt);
   }
 };
 

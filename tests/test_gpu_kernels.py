@@ -374,8 +374,12 @@ def test_swiglu_f32(n, d, dff):
     assert max_rel_floor(out, ref) <= 1e-4
 
 
-@pytest.mark.parametrize("n,d,dff", [(300, 512, 1000), (600, 512, 1000), (64, 4096, 14336), (1, 256, 64)])
+@pytest.mark.parametrize("n,d,dff", [(300, 512, 1000), (600, 512, 1000), (64, 4096, 14336), (1, 256, 64),
+                                     (1024, 4096, 2048), (2048, 4096, 11008)])
 def test_swiglu_bf16(n, d, dff):
+    """Includes shapes with too few 256x256 tiles for the GPU, whose K is split
+    over workgroups (1024 x 4096 x 2048: gate/up in 4 splits, down in 2; the
+    Llama-7B FFN at 2048 tokens: down in 2)."""
     x = synth.normal(110, (n, d), dtype="bf16")
     wg = synth.normal(111, (dff, d), 0.02, dtype="bf16")
     wu = synth.normal(112, (dff, d), 0.02, dtype="bf16")
