@@ -690,20 +690,21 @@ gemm_mfma_dma_kernel(BufOperands op, int M, int N, int K, int kps, int tiles_m, 
   auto kstep = [&](int kt, auto CUR) {
     constexpr int cur = decltype(CUR)::value;
     using NXT = std::integral_constant<int, 1 - cur>;
+    // the 16 loads spread over sub-steps 0..2, one after every third MFMA,
+    // so they reach the texture addresser no faster than it drains them
     auto sub = [&](auto F, auto NF, int s) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < 16; ++t) {
         mf(F, t);
-        if (s < 2) {
-          dma(NXT{}, kt + 1, 8 * s + t);
+        const int slot = 16 * s + t;
+        if (slot % 3 == 0 && slot / 3 < 16) {
+          dma(NXT{}, kt + 1, slot / 3);
           fence();
         }
-      }
-#pragma unroll
-      for (int t = 8; t < 16; ++t) {
-        mf(F, t);
-        rd(CUR, s + 1, NF, t - 8);
-        fence();
+        if (t >= 8) {
+          rd(CUR, s + 1, NF, t - 8);
+          fence();
+        }
       }
     };
     sub(I0{}, I1{}, 0);
