@@ -4,8 +4,9 @@ Gates (the readings of the stated tolerances):
   * fp32 path: max relative error (floored at 1e-3 of the tensor's max) <= 1e-4;
   * bf16 path: relative Frobenius error <= 1e-2 against the exact fp64 oracle,
     and max abs error <= 5e-2 against the bf16 storage-point oracle, on the
-    block output y (fp32 residual stream).  The sublayer deltas h - x and
-    y - h are reported beside them.
+    block output y (fp32 residual stream); the same relative Frobenius gate
+    on the block's whole delta y - x and on the attention sublayer's h - x
+    (h from a run with W_down = 0).
 """
 
 import numpy as np
@@ -44,15 +45,32 @@ def oracle_block(inp, storage=False):
                                 return_intermediates=True)
 
 
+def gpu_h(inp):
+    """The GPU's residual stream after attention, h: the block run again with
+    W_down = 0, where y = h + 0 exactly."""
+    inp0 = synth.make_block_inputs(inp.wl)
+    inp0.weights["w_down"] = torch.zeros_like(inp0.weights["w_down"])
+    h, _, _ = run_block(inp0)
+    return h
+
+
 def check_bf16(name, y, inp):
+    """y against both oracles, and the two sublayer deltas on their own: the
+    residual x dominates y (|x| ~ 1 where the attention delta's rms can be
+    ~0.03), so a y-level relF alone would hardly see a wrong sublayer."""
     y_ex, inter = oracle_block(inp)
     y_st, _ = oracle_block(inp, storage=True)
     report(f"{name} vs exact", y, y_ex)
     report(f"{name} vs storage", y, y_st)
     x64 = to64(inp.x)
+    h = to64(gpu_h(inp))
+    h_ex = inter["h"]
     report(f"{name} delta y-x", to64(y) - x64, y_ex - x64)
+    report(f"{name} attention delta h-x", h - x64, h_ex - x64)
     assert rel_frobenius(y, y_ex) <= 1e-2
     assert max_abs(y, y_st) <= 5e-2
+    assert rel_frobenius(to64(y) - x64, y_ex - x64) <= 1e-2
+    assert rel_frobenius(h - x64, h_ex - x64) <= 1e-2
 
 
 def test_toy_block_f32():
@@ -162,14 +180,19 @@ def test_decode_workload_sampled():
     sub = lambda a: a[sel]
     args = (sub(f["x"]), f["w"], sub(f["positions"]), wl.theta, wl.eps, wl.n_q, wl.n_kv,
             sub(f["k_cache"]), sub(f["v_cache"]))
-    y_ex = oracle.block_forward(*args)
+    y_ex, inter = oracle.block_forward(*args, return_intermediates=True)
     y_st = oracle.block_forward(*args, bf16_storage=True)
     got = to64(y)[sel]
+    h = to64(gpu_h(inp))[sel]
+    x_sel = sub(f["x"])
     report("decode full vs exact", got, y_ex)
     report("decode full vs storage", got, y_st)
-    report("decode full delta", got - sub(f["x"]), y_ex - sub(f["x"]))
+    report("decode full delta", got - x_sel, y_ex - x_sel)
+    report("decode attention delta h-x", h - x_sel, inter["h"] - x_sel)
     assert rel_frobenius(got, y_ex) <= 1e-2
     assert max_abs(got, y_st) <= 5e-2
+    assert rel_frobenius(got - x_sel, y_ex - x_sel) <= 1e-2
+    assert rel_frobenius(h - x_sel, inter["h"] - x_sel) <= 1e-2
     # slot 4096 now holds the new rotated k and v; earlier slots untouched
     assert torch.equal(kc[:, :4096].cpu(), inp.k_cache[:, :4096])
     assert torch.count_nonzero(kc[:, 4096]) > 0
@@ -183,13 +206,22 @@ def test_prefill_workload_sampled_rows():
     rows = [(0, 0), (0, 1), (0, 63), (0, 64), (0, 1000), (0, 4095), (0, 4096), (0, 8190), (0, 8191)]
     f = inp.as_f64()
     args = (f["x"], f["w"], f["positions"], rows, wl.theta, wl.eps, wl.n_q, wl.n_kv)
-    y_ex, _ = oracle.block_forward_rows(*args)
+    y_ex, h_ex = oracle.block_forward_rows(*args)
     y_st, _ = oracle.block_forward_rows(*args, bf16_storage=True)
     got = np.stack([to64(y[b, t]) for b, t in rows])
+    del y
+    h_all = gpu_h(inp)
+    h = np.stack([to64(h_all[b, t]) for b, t in rows])
+    del h_all
+    x_rows = np.stack([f["x"][b, t] for b, t in rows])
     report("prefill full vs exact", got, y_ex)
     report("prefill full vs storage", got, y_st)
+    report("prefill full delta", got - x_rows, y_ex - x_rows)
+    report("prefill attention delta h-x", h - x_rows, h_ex - x_rows)
     assert rel_frobenius(got, y_ex) <= 1e-2
     assert max_abs(got, y_st) <= 5e-2
+    assert rel_frobenius(got - x_rows, y_ex - x_rows) <= 1e-2
+    assert rel_frobenius(h - x_rows, h_ex - x_rows) <= 1e-2
 
 
 _mha_cache = {}
