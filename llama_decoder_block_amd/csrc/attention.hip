@@ -7,15 +7,18 @@
 //
 // attn_flash_kernel (bf16, hd = 128, prefill): one workgroup per (sequence,
 //   KV group, tile of 128 query rows) where the rows are the R = n_q/n_kv
-//   heads of the group times 128/R tokens.  Each K/V tile of 64 slots is
-//   staged once in LDS and used by all R heads.  Four wavefronts own 32 query
-//   rows each.  Scores are computed transposed (S^T = K Q^T on
-//   v_mfma_f32_32x32x16_bf16) so that every lane holds 32 scores of ONE query
-//   row: the online-softmax max/sum need only one cross-lane exchange, and the
-//   probabilities already sit in the register layout of the B operand of
-//   O^T = V^T P^T.  V is written to LDS transposed for that product.
-//   Accumulators, running max and sum are fp32; P is rounded to bf16 for the
-//   MFMA.  Only tiles at or below each workgroup's last visible slot are read.
+//   heads of the group times 128/R tokens.  Each K/V tile of 64 slots goes
+//   once from HBM straight into LDS (buffer loads with LDS destination) and
+//   is used by all R heads.  Four wavefronts own 32 query rows each.  Scores
+//   are computed transposed (S^T = K Q^T on v_mfma_f32_32x32x16_bf16) so that
+//   every lane holds 32 scores of ONE query row: the online-softmax max/sum
+//   need only one cross-lane exchange, and the probabilities already sit in
+//   the register layout of the B operand of O^T = V^T P^T, whose A operand
+//   comes from V's [slot][hd] tile through transposing LDS reads
+//   (ds_read_b64_tr_b16).  S^T of tile j+1 is issued beside the softmax of
+//   tile j.  Accumulators, running max and sum are fp32; P is rounded to bf16
+//   for the MFMA.  Only tiles at or below each workgroup's last visible slot
+//   are read.
 // attn_decode3_kernel (bf16, hd = 128, one query token per sequence): one
 //   workgroup per (sequence, KV group) whose wavefronts split the visible
 //   slots; each streams its K/V rows once for the R query heads of the group
@@ -29,6 +32,7 @@
 // attn_valu_kernel: generic fp32-accumulating kernel (one wavefront per query
 //   row, online softmax over 64-slot chunks) for fp32 and other shapes.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -111,18 +115,35 @@ attn_valu_kernel(AttnArgs a) {
 constexpr int kFHd = 128;
 constexpr int kFRows = 128;              // query rows per workgroup
 constexpr int kFKeys = 64;               // key slots per tile
-constexpr int kKStride = kFHd * 2 + 16;  // bytes per K row in LDS (padded)
-constexpr int kVStride = kFKeys * 2 + 16; // bytes per V^T row in LDS (padded, 16-byte aligned)
-constexpr int kKBytes = kFKeys * kKStride;
-constexpr int kVBytes = kFHd * kVStride;
-constexpr int kFBufBytes = kKBytes + kVBytes;
+constexpr int kTileBytes = kFKeys * kFHd * 2;  // one K or V tile: 64 slots x 256 bytes
+
+// LDS layout of a K or V tile: four column blocks of 32 hd (64 bytes of each
+// slot row), block-major, slot rows of 64 bytes inside a block.  In K tiles
+// the 16-byte chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so the 16
+// rows read by 16 lanes at one logical chunk fall on 16 distinct bank groups;
+// V tiles are unswizzled (a transposing read takes 8 consecutive rows x 64
+// bytes, a contiguous 512 bytes).
+__device__ __forceinline__ int kswz(int r) { return (r >> 2) & 3; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
 
 template <int R>
 __global__ void __launch_bounds__(256, 2)
 attn_flash_kernel(AttnArgs a, int n_qtiles) {
   constexpr int TQ = kFRows / R;  // tokens per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kFBufBytes];
+  // two K and two V tiles, as four arrays so that every access names its
+  // buffer at compile time
+  __shared__ __attribute__((aligned(1024))) uint8_t k0s[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1s[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0s[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v1s[kTileBytes];
   __shared__ int vis_s[kFRows];
+  auto kbuf = [&](auto I) -> uint8_t* { if constexpr (decltype(I)::value == 0) return k0s; else return k1s; };
+  auto vbuf = [&](auto I) -> uint8_t* { if constexpr (decltype(I)::value == 0) return v0s; else return v1s; };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   // Heavy tiles (late query tokens) first across all (sequence, KV group)
   // pairs, so the last workgroups to start are the light ones; consecutive
@@ -132,14 +153,14 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
   const int qt = n_qtiles - 1 - static_cast<int>(blockIdx.x) / n_bg;
   const int bg = static_cast<int>(blockIdx.x) % n_bg;
   const int g = bg % a.nkv, b = bg / a.nkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = qt * TQ;
   const int my_row = w * 32 + (lane & 31);
   const int my_hi = my_row / TQ, my_t = t0 + my_row % TQ;
   const int my_h = g * R + my_hi;
   const int half = lane >> 5;
 
-  // Q fragments: B operand, column = query row, k = hd
   bf16x8 qf[8];
   {
     const int tq = min(my_t, a.Tq - 1);
@@ -150,8 +171,7 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
       qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + half * 8);
     // Consume the Q fragments before the tile loop, so their wait is not
     // placed inside it, where (the counter being in order) it would also
-    // wait for the next tile's K/V.  Issued first, they share the latency of
-    // the position loads below.
+    // wait for the next tile's loads.
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(qf[kk]));
   }
@@ -175,73 +195,58 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
   }
   const int nkt = maxvis < 0 ? 0 : maxvis / kFKeys + 1;
 
-  const int64_t kvrow = static_cast<int64_t>(a.nkv) * kFHd;  // elements between slots
+  const int64_t kvrow = static_cast<int64_t>(a.nkv) * kFHd;
   const bf16_t* kbase = static_cast<const bf16_t*>(a.k) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * kFHd;
   const bf16_t* vbase = static_cast<const bf16_t*>(a.v) + (static_cast<int64_t>(b) * a.S * a.nkv + g) * kFHd;
-
-  // global -> register staging: K: 4 rows x 16 B per thread; V: 4 slots x 8 hd.
-  // Loads go through buffer resources based at this (sequence, KV head):
-  // the lane's byte offset stays in a VGPR, the tile's in an SGPR.
-  const int k_chunk = tid & 15, k_row = tid >> 4;     // rows k_row + 16 i
-  const int v_kg = tid & 15, v_hc = tid >> 4;         // slots 4*v_kg..+3, hd 8*v_hc..+7
-  u32x4 kreg[4], vreg[4];
   const uint32_t kv_bytes = static_cast<uint32_t>((static_cast<int64_t>(a.S - 1) * kvrow + kFHd) * 2);
   const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kbase, kv_bytes);
   const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vbase, kv_bytes);
   const uint32_t row_bytes = static_cast<uint32_t>(kvrow) * 2;
-  uint32_t koff[4], voff[4];  // byte offsets of this thread's K rows / V slots within a tile
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    koff[i] = (k_row + 16 * i) * row_bytes + k_chunk * 16;
-    voff[i] = (4 * v_kg + i) * row_bytes + v_hc * 16;
-  }
-  auto gload = [&](int kt) {
+
+  // Tile loads: wavefront w fills column block w (bytes 64 w .. 64 w + 63
+  // of each slot row), 16 rows per instruction; lane i writes LDS chunk i % 4
+  // of row 16 q + i / 4, i.e. the logical chunk (i % 4) ^ swizzle, where the K
+  // swizzle of that row, (row >> 2) & 3, is i / 16 for every q.
+  const uint32_t kvo = (lane >> 2) * row_bytes + static_cast<uint32_t>(((lane & 3) ^ (lane >> 4)) << 4);
+  const uint32_t vvo = (lane >> 2) * row_bytes + static_cast<uint32_t>((lane & 3) << 4);
+  auto tile_load = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo, uint8_t* dst, bool ktile, int kt) {
     const int base = kt * kFKeys;
+    lds_byte* d = (lds_byte*)(dst + w * 4096);
     if (base + kFKeys - 1 <= maxvis) {
-      const uint32_t soff = static_cast<uint32_t>(base) * row_bytes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kreg[i] = buffer_load16(krsrc, koff[i], soff);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = buffer_load16(vrsrc, voff[i], soff);
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t soff = static_cast<uint32_t>(base + 16 * q) * row_bytes + static_cast<uint32_t>(w * 64);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(d + q * 1024), 16,
+                                                 vo, soff, 0, 0);
+      }
     } else {
       // the tile holding the workgroup's last visible slot: later slots are
       // read as that slot (their weights are exactly 0, and a cache row past
       // the written positions may hold anything, NaN included)
+      const int lc = ktile ? ((lane & 3) ^ (lane >> 4)) : (lane & 3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t j = static_cast<uint32_t>(min(base + k_row + 16 * i, maxvis));
-        kreg[i] = buffer_load16(krsrc, j * row_bytes + k_chunk * 16, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t j = static_cast<uint32_t>(min(base + 4 * v_kg + i, maxvis));
-        vreg[i] = buffer_load16(vrsrc, j * row_bytes + v_hc * 16, 0);
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t j = static_cast<uint32_t>(min(base + 16 * q + (lane >> 2), maxvis));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(d + q * 1024), 16,
+                                                 j * row_bytes + static_cast<uint32_t>(w * 64 + (lc << 4)), 0, 0, 0);
       }
     }
   };
-  auto lstore = [&](int buf) {
-    uint8_t* kb = smem + buf * kFBufBytes;
-    uint8_t* vb = kb + kKBytes;
+
+  // K fragment of chunk kk (hd 16 kk + 8 half .. + 7, logical chunk
+  // 2 (kk % 2) + half of block kk / 2) of row h2 * 32 + lane % 32: a per-lane
+  // offset for even and odd kk, the rest immediate.
+  uint32_t ka[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(kb + (k_row + 16 * i) * kKStride + k_chunk * 16) = kreg[i];
-    // transpose 4 slots x 8 hd into 8 rows (hd) of 4 slots: output word
-    // (slot pair, hd e) takes the same 16-bit half of two input words.
-    // Within each 16-slot block the 4-slot groups are stored in the order
-    // 0, 2, 1, 3, so that the 8 slots one lane multiplies in the PV product
-    // (4s..4s+3 and 8+4s..8+4s+3 for lane half s) are 16 contiguous bytes.
-    const int v_grp = v_kg & 3;
-    const int v_pos = ((v_kg >> 2) * 16 + ((v_grp & 1) << 3) + ((v_grp & 2) << 1)) * 2;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u32x2 lo = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u),
-                        __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u)};
-      const u32x2 hi = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u),
-                        __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u)};
-      *reinterpret_cast<u32x2*>(vb + (v_hc * 8 + 2 * w) * kVStride + v_pos) = lo;
-      *reinterpret_cast<u32x2*>(vb + (v_hc * 8 + 2 * w + 1) * kVStride + v_pos) = hi;
-    }
-  };
+  for (int o = 0; o < 2; ++o)
+    ka[o] = static_cast<uint32_t>((lane & 31) * 64 + (((2 * o + half) ^ kswz(lane & 31)) << 4));
+  // V^T fragment of hd block d for the 16 slots of (h2, hh): two transposing
+  // reads r = 0, 1 of 4 slots each (slots 16 hh + 8 r + 4 half + 0..3 of the
+  // 32-slot half h2, the order in which this lane holds the weights); source
+  // lane i of each 16-lane group reads slot + i / 4, hd 16 ((lane / 16) % 2)
+  // + 4 (i % 4) .. + 3 of block d.
+  const uint32_t va = static_cast<uint32_t>((4 * half + ((lane & 15) >> 2)) * 64 + 32 * ((lane >> 4) & 1) +
+                                            8 * (lane & 3));
 
   f32x16 oacc[4];
 #pragma unroll
@@ -251,35 +256,41 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale * kLog2e;
 
-  if (nkt > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-    const uint8_t* kb = smem + buf * kFBufBytes;
-    const uint8_t* vb = kb + kKBytes;
-
-    // S^T = K Q^T for two 32-slot halves
-    // the two 32-slot halves alternate so consecutive MFMAs are independent
-    f32x16 sacc[2];
+  // S^T = K Q^T of one tile from K buffer KB (the two 32-slot halves
+  // alternate so consecutive MFMAs are independent)
+  auto qk = [&](auto KB, f32x16 (&s)[2]) {
+    const uint8_t* kb = kbuf(KB);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.f;
+      for (int e = 0; e < 16; ++e) s[h2][e] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            kb + (h2 * 32 + (lane & 31)) * kKStride + kk * 32 + half * 16);
-        sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[h2], 0, 0, 0);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + (kk >> 1) * 4096 + h2 * 2048 + ka[kk & 1]);
+        s[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[h2], 0, 0, 0);
       }
-    // Raw-score maximum of the tile (the scale c > 0 preserves order); keys
-    // past a query's position are masked only on tiles that reach the
-    // diagonal of some row of this wavefront (wave-uniform test).
+  };
+  auto wait_all_barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One tile kt whose scores sit in `cur`: the loads of K kt + 2 and V kt + 1,
+  // masking, the running maximum and rescale, then S^T of tile kt + 1 into
+  // `nxt` beside the weights of tile kt, and O^T += V^T P^T.  Buffers: K kt in
+  // KB P (free: its scores were computed a tile earlier), K kt + 1 in KB 1-P,
+  // V kt in VB P, V kt + 1 into VB 1-P (free since the previous tile).
+  auto step = [&](int kt, auto P, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto NEXT) {
+    constexpr int p = decltype(P)::value;
+    constexpr bool next = decltype(NEXT)::value;
+    using NP = std::integral_constant<int, 1 - p>;
+    wait_all_barrier();
+    if (kt + 2 < nkt) tile_load(krsrc, kvo, kbuf(P), true, kt + 2);
+    if (kt + 1 < nkt) tile_load(vrsrc, vvo, vbuf(NP{}), false, kt + 1);
+
     const bool need_mask = kt * kFKeys + kFKeys - 1 > wave_min;
     if (need_mask) {
 #pragma unroll
@@ -287,14 +298,14 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int j = kt * kFKeys + h2 * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-          if (j > my_vis) sacc[h2][e] = -INFINITY;
+          if (j > my_vis) cur[h2][e] = -INFINITY;
         }
     }
     float tmax = -INFINITY;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[h2][e]);
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, cur[h2][e]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
     // Online softmax: whenever the tile raises some row's maximum, every row
     // of the wavefront moves its reference m_run to its running maximum
@@ -314,6 +325,9 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
     }
+
+    if constexpr (next) qk(NP{}, nxt);
+
     const float neg_m = -m_run;
     float psum = 0.f;
     bf16x8 pf[2][2];
@@ -324,8 +338,8 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
         u32x4 pk;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = fast_exp2(__builtin_fmaf(sacc[h2][hh * 8 + 2 * e2], c, neg_m));
-          const float p1 = fast_exp2(__builtin_fmaf(sacc[h2][hh * 8 + 2 * e2 + 1], c, neg_m));
+          const float p0 = fast_exp2(__builtin_fmaf(cur[h2][hh * 8 + 2 * e2], c, neg_m));
+          const float p1 = fast_exp2(__builtin_fmaf(cur[h2][hh * 8 + 2 * e2 + 1], c, neg_m));
           psum += p0 + p1;
           pk[e2] = pack_bf16x2(p0, p1);
         }
@@ -333,25 +347,46 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
       }
     l_run += psum;
 
-    // O^T += V^T P^T
+    const uint8_t* vb = vbuf(P);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int s0 = h2 * 32 + hh * 16 + half * 8;  // stored position of this lane's 8 slots
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const uint8_t* vr = vb + (d * 32 + (lane & 31)) * kVStride;
-          const u32x4 vv = *reinterpret_cast<const u32x4*>(vr + s0 * 2);
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                            pf[h2][hh], oacc[d], 0, 0, 0);
+          lds_byte* vt = (lds_byte*)vb + d * 4096 + (h2 * 32 + hh * 16) * 64 + va;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)vt);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vt + 8 * 64));
+          const s16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[h2][hh], oacc[d],
+                                                            0, 0, 0);
         }
-      }
-    if (kt + 1 < nkt) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  f32x16 sa[2], sb[2];
+  if (nkt > 0) {
+    tile_load(krsrc, kvo, k0s, true, 0);
+    tile_load(vrsrc, vvo, v0s, false, 0);
+    if (nkt > 1) tile_load(krsrc, kvo, k1s, true, 1);
+    wait_all_barrier();
+    qk(I0{}, sa);
+  }
+  // tile kt (even) starts with its scores in sa and its K/V in buffers 0
+  using Yes = std::true_type;
+  using No = std::false_type;
+  int kt = 0;
+  for (; kt + 2 < nkt; kt += 2) {
+    step(kt, I0{}, sa, sb, Yes{});
+    step(kt + 1, I1{}, sb, sa, Yes{});
+  }
+  if (kt + 1 < nkt) {
+    step(kt, I0{}, sa, sb, Yes{});
+    step(kt + 1, I1{}, sb, sa, No{});
+  } else if (kt < nkt) {
+    step(kt, I0{}, sa, sb, No{});
   }
 
-  // normalise and store: O^T register e of subtile d is hd = d*32 + (e/4)*8 + half*4 + e%4
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (my_t < a.Tq && my_vis >= 0) {
     const float inv = 1.f / l_tot;
