@@ -4,10 +4,9 @@ outputs on the same seeded inputs as the GPU tests (all zeros, one dropped
 32-slot step, every eighth step dropped, an off-by-one visible length).
 
 The fp32 evaluations follow the steps the bound is derived from: bf16 inputs,
-fp32 scores, an integer row offset (the prefill kernel) or the running
-maximum, exp2 in fp32, weights rounded to bf16 (prefill) or kept in fp32
-(decode), fp32 sums chunk by chunk with the chunks merged by rescaling, one
-division and one rounding to bf16.  They stand in for a correct kernel; the
+fp32 scores, the running maximum as the row offset, exp2 in fp32, weights
+rounded to bf16 (prefill) or kept in fp32 (decode), fp32 sums chunk by chunk
+with the chunks merged by rescaling, one division and one rounding to bf16.  They stand in for a correct kernel; the
 planted mistakes stand in for wrong ones.
 """
 
@@ -43,7 +42,7 @@ def emulate(q, k, v, vis, bf16_weights, chunk=256):
                     kk, vv = k[b, j0:min(n, j0 + chunk), gi], v[b, j0:min(n, j0 + chunk), gi]
                     s = (kk @ q[b, t, h]).astype(F32)
                     cm = F32(s.max() * c)
-                    m_new = F32(math.ceil(max(m_run, cm))) if bf16_weights else F32(max(m_run, cm))
+                    m_new = F32(max(m_run, cm))
                     alpha = F32(np.exp2(F32(m_run - m_new))) if np.isfinite(m_run) else F32(0.0)
                     p = np.exp2((s * c - m_new).astype(F32)).astype(F32)
                     pw = oracle.round_bf16(p).astype(F32) if bf16_weights else p
@@ -59,8 +58,8 @@ def fails(got, ref, bound):
 
 
 def test_bound_admits_fp32_prefill_and_decode_arithmetic():
-    """Prefill-shaped (bf16 weights, integer offsets, 64-slot tiles) and
-    decode-shaped (fp32 weights, 256-slot chunks) evaluations stay inside."""
+    """Prefill-shaped (bf16 weights, 64-slot tiles) and decode-shaped (fp32
+    weights, 256-slot chunks) evaluations stay inside."""
     q, k, v = attn_inputs(50, 1, 200, 200, 8, 2, 128, "bf16")
     vis = np.arange(200)[None, :]
     ref, bound = attention_with_bound(q, k, v, vis, bf16_weights=True)
