@@ -301,23 +301,27 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
           if (j > my_vis) cur[h2][e] = -INFINITY;
         }
     }
+    // From here to the end of the tile the code is one basic block, so the
+    // next tile's score MFMAs interleave with this tile's maximum and
+    // rescale, and the PV MFMAs with the weights.
+    if constexpr (next) qk(NP{}, nxt);
     float tmax = -INFINITY;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, cur[h2][e]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
-    // Online softmax: whenever the tile raises some row's maximum, every row
-    // of the wavefront moves its reference m_run to its running maximum
-    // (rows whose maximum did not move rescale by exactly 1).  The weights
-    // exp2(score * c - m_run) are rounded to bf16 for the PV product, so a
-    // reference equal to the row maximum keeps the largest weight exactly 1
-    // and free of rounding error, as in the softmax that subtracts the row
-    // maximum; only weights of tiles seen before the maximum are rounded
-    // against an earlier reference.
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run) != 0) {
+    // Online softmax: each row's reference m_run is its running maximum
+    // (rows whose maximum did not move rescale by exactly exp2(0) = 1).  The
+    // weights exp2(score * c - m_run) are rounded to bf16 for the PV product,
+    // so a reference equal to the row maximum keeps the largest weight
+    // exactly 1 and free of rounding error, as in the softmax that subtracts
+    // the row maximum; only weights of tiles seen before the maximum are
+    // rounded against an earlier reference.  (A row with nothing visible yet
+    // keeps -inf, and its factor 1 leaves its zero accumulators at zero.)
+    {
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = fast_exp2(m_run - m_new);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -325,8 +329,6 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
     }
-
-    if constexpr (next) qk(NP{}, nxt);
 
     const float neg_m = -m_run;
     float psum = 0.f;
