@@ -12,7 +12,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libllama_block.so")
+# LLAMA_BLOCK_LIB selects another build of the same library (the tests use a
+# host-AddressSanitizer build of it); by default the in-tree build is loaded
+LIB_PATH = os.environ.get("LLAMA_BLOCK_LIB") or os.path.join(_PKG, "lib", "libllama_block.so")
 
 F32, BF16 = 0, 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "workspace too small", -4: "hip error"}
