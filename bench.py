@@ -19,6 +19,9 @@ roofline   = the dominant kernel (fused gate/up GEMM + SiLU product):
              same kernel, calibrated by a plain 1 GiB copy in the same passes
 mha_prefill = the Llama-7B and Llama-65B MHA prefill workloads, timed like
              the headline prefill, against their 60%-of-peak target times
+tp8_shard_prefill = one GPU's share of the headline prefill under 8-way
+             tensor parallelism (4 query heads, 1 KV head, d_ff 1792), the
+             all-reduces left out
 kernels    = every timed step of the path: launches, average time, and the
              achieved TFLOP/s (GEMMs, attention) or GB/s (norms)
 decode     = the decode step (1 GiB read between steps so that weights and
@@ -55,6 +58,7 @@ PREFILL = "llama3_8b_gqa_prefill"
 DECODE = "llama3_8b_gqa_decode"
 DOMINANT = "gate_up_silu/gemm_mfma_gate_up_silu"
 DECODE_ATTN = "attention/attn_decode_wg"
+PREFILL_TP8 = {"n_q": 4, "n_kv": 1, "d_ff": 1792}  # one GPU's share of 8-way tensor parallelism
 MHA_TARGET_MS = {"llama7b_mha_prefill": 0.572, "llama65b_mha_prefill": 8.966}  # 60% of the bf16 MFMA peak
 
 
@@ -625,6 +629,41 @@ def bench_mha_prefill(name, dev, args):
     return out
 
 
+def bench_tp8_shard(dev, args):
+    """One GPU's share of the Llama-3-8B prefill under 8-way tensor
+    parallelism by KV group: the block's kernels with 4 query heads, 1 KV
+    head and d_ff = 14336 / 8 = 1792 (QKV N = 768, o K = 512, gate/up
+    N = 2 x 1792, down K = 1792), at T = 8192.  The two all-reduces of [8192,
+    4096] that the sharded block adds (after o and after down) are not part
+    of it; this times the kernels at the shard's real shapes."""
+    wl = synth.workload(PREFILL, n_q=PREFILL_TP8["n_q"], n_kv=PREFILL_TP8["n_kv"], d_ff=PREFILL_TP8["d_ff"])
+    x, w, pos = gpu_block_inputs(wl, dev)
+    need = binding.block_workspace_bytes(wl.batch, wl.seq, wl.d_model, wl.n_q, wl.n_kv, wl.head_dim, wl.d_ff, 0,
+                                         binding.BF16, binding.F32)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+
+    def step():
+        binding.block_forward(x, w, pos, wl.n_q, wl.n_kv, wl.theta, wl.eps, y=y, workspace=ws)
+    ms, per, kernels = time_steps(step, args.steps, args.warmup)
+    sh = shape_of(wl)
+    flops = wm.prefill_flops(sh, wl.batch, wl.seq)
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] tp8 shard of {PREFILL}: {ms:.3f} ms/step, {tf:.1f} TFLOP/s ({tf / MFMA_BF16_PEAK_TFLOPS:.1%} "
+        f"of peak)")
+    table = kernel_table(kernels, wm.step_work(sh, wl.batch, wl.seq))
+    for k, row in table.items():
+        log(f"[bench]   {k:40s} {row}")
+    out = {"workload": f"{PREFILL} shard of 8-way tensor parallelism: B={wl.batch} T={wl.seq} d={wl.d_model} "
+                       f"n_q={wl.n_q} n_kv={wl.n_kv} hd={wl.head_dim} d_ff={wl.d_ff} theta={wl.theta:g} "
+                       f"(all-reduces not included), weights drawn on the GPU",
+           "ms_per_step": round(ms, 4), "ms_median": round(per[len(per) // 2], 4), "flops": flops,
+           "tflops": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "kernels": table}
+    del step, x, w, pos, ws, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -697,6 +736,7 @@ def main():
     rope = bench_rope(wl, dev, args)
     chunked = bench_chunked_prefill(wl, dev, args)
     mha = {n: bench_mha_prefill(n, dev, args) for n in MHA_TARGET_MS}
+    tp8 = bench_tp8_shard(dev, args)
 
     # ---------------- decode -----------------
     decode = None
@@ -807,6 +847,7 @@ def main():
                                 if traffic and "fetch_scale" in traffic else None),
         "chunked_prefill": chunked,
         "mha_prefill": mha,
+        "tp8_shard_prefill": tp8,
         "decode": decode,
         "device": device,
         "hbm_copy": copy_bw,

@@ -224,6 +224,34 @@ def test_prefill_workload_sampled_rows():
     assert rel_frobenius(h - x_rows, h_ex - x_rows) <= 1e-2
 
 
+def test_tp8_shard_sampled_rows():
+    """One GPU's share of the Llama-3-8B prefill under 8-way tensor
+    parallelism (4 query heads, 1 KV head, d_ff 1792, T = 8192): the QKV
+    product (N = 768, K split over workgroups), o at K = 512 and the FFN at
+    d_ff 1792, sampled rows against the oracle with the sublayer gates."""
+    wl = synth.workload("llama3_8b_gqa_prefill", n_q=4, n_kv=1, d_ff=1792)
+    inp = synth.make_block_inputs(wl)
+    y, _, _ = run_block(inp)
+    rows = [(0, 0), (0, 63), (0, 64), (0, 4095), (0, 4096), (0, 8191)]
+    f = inp.as_f64()
+    args = (f["x"], f["w"], f["positions"], rows, wl.theta, wl.eps, wl.n_q, wl.n_kv)
+    y_ex, h_ex = oracle.block_forward_rows(*args)
+    y_st, _ = oracle.block_forward_rows(*args, bf16_storage=True)
+    got = np.stack([to64(y[b, t]) for b, t in rows])
+    del y
+    h_all = gpu_h(inp)
+    h = np.stack([to64(h_all[b, t]) for b, t in rows])
+    del h_all
+    x_rows = np.stack([f["x"][b, t] for b, t in rows])
+    report("tp8 shard vs exact", got, y_ex)
+    report("tp8 shard vs storage", got, y_st)
+    report("tp8 shard attention delta h-x", h - x_rows, h_ex - x_rows)
+    assert rel_frobenius(got, y_ex) <= 1e-2
+    assert max_abs(got, y_st) <= 5e-2
+    assert rel_frobenius(got - x_rows, y_ex - x_rows) <= 1e-2
+    assert rel_frobenius(h - x_rows, h_ex - x_rows) <= 1e-2
+
+
 _mha_cache = {}
 
 
