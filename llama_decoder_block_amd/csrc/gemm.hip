@@ -244,6 +244,14 @@ gemm_mfma_kernel(const bf16_t* __restrict__ X, WRows<bf16_t> W, int M, int N, in
   }
 }
 
+// a per-row key of lane t of the wavefront (32- or 64-bit)
+__device__ __forceinline__ int shfl_key(int k, int t) { return __shfl(k, t, 64); }
+__device__ __forceinline__ int64_t shfl_key(int64_t k, int t) {
+  const int lo = __shfl(static_cast<int>(k & 0xffffffff), t, 64);
+  const int hi = __shfl(static_cast<int>(k >> 32), t, 64);
+  return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo));
+}
+
 // ---------------------------------------------------------------------------
 // Epilogue of the 256 x 256 tile kernels (4 wavefronts in a 2 x 2 grid, each
 // holding 4 x 4 accumulator tiles of 32 x 32): register e of a 32x32 tile is
@@ -279,13 +287,16 @@ __device__ __forceinline__ void tile_epilogue(const f32x16 (&acc)[4][4], u32x4* 
       const int g = le & 31, hsel = le >> 5, srow = le & 31, shalf = le >> 5;
       const int n = out_n0 + wave_n * WN + g * 4;
       const int mw = m0 + wave_m * WM;
-      int key[TM];
+      // what depends on this lane's column group only, resolved once
+      const typename Epi::Col col = epi.col(n);
+      using Key = typename Epi::Key;
+      Key key[TM];
 #pragma unroll
-      for (int b = 0; b < TM; ++b) key[b] = Epi::kRowKey ? epi.row_key(mw + b * 32 + g) : 0;
+      for (int b = 0; b < TM; ++b) key[b] = Epi::kRowKey ? epi.row_key(mw + b * 32 + g) : Key{};
       // row of token 2i + hsel of block b (iteration i: lanes 0-31 one token, 32-63 the next)
       auto row_of = [&](int b, int i) {
         const int t = 2 * i + hsel;
-        return epi.row_from(mw + b * 32 + t, Epi::kRowKey ? __shfl(key[b], t, 64) : 0);
+        return epi.row_from(mw + b * 32 + t, Epi::kRowKey ? shfl_key(key[b], t) : Key{});
       };
       // chunks of CH iterations (16 / CH per block); chunk c + 1's pre()
       // loads are issued before chunk c is stored.  CH is the largest that
@@ -294,7 +305,7 @@ __device__ __forceinline__ void tile_epilogue(const f32x16 (&acc)[4][4], u32x4* 
       f32x4 pre[2][CH];
       auto issue = [&](int c) {
 #pragma unroll
-        for (int i = 0; i < CH; ++i) pre[c & 1][i] = epi.pre(row_of(c / NCH, (c % NCH) * CH + i), n);
+        for (int i = 0; i < CH; ++i) pre[c & 1][i] = epi.pre(row_of(c / NCH, (c % NCH) * CH + i), col);
       };
       issue(0);
       // chunk c's accumulator tile acc[.][c / NCH] must be a compile-time
@@ -324,7 +335,7 @@ __device__ __forceinline__ void tile_epilogue(const f32x16 (&acc)[4][4], u32x4* 
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
           const float v[4] = {val[i][0], val[i][1], val[i][2], val[i][3]};
-          epi.put(row_of(b, i0 + i), n, pre[c & 1][i], v);
+          epi.put(row_of(b, i0 + i), col, pre[c & 1][i], v);
         }
       });
       return;

@@ -33,14 +33,16 @@ struct WSeg {
 // epilogue receives the gate and up accumulators of the same column c.
 //
 // The single-operand epilogues also offer a split form for whole groups of
-// four columns (when vec_ok()): row(m) gathers what depends on the row only,
-// pre(row, n) issues the group's loads (or computes its factors), and
-// put(row, n, pre, v) finishes and stores.  A tile epilogue issues pre() for
-// many groups before the first put(), so their loads are in flight together
-// instead of one load-use-store round trip per group.  row(m) is also
-// available as row_from(m, row_key(m)), where row_key(m) is the one per-row
-// value read from memory (0 when there is none), so that a tile can load the
-// keys of all its rows at once and share them between lanes.
+// four columns (when vec_ok()): col(n) resolves what depends on the column
+// group only, row_from(m, row_key(m)) what depends on the row only,
+// pre(row, col) issues the group's loads (or computes its factors), and
+// put(row, col, pre, v) finishes and stores.  A tile epilogue resolves its
+// lane's column once, computes row_key() once per row in the lane that owns
+// the row and shares it between lanes, and issues pre() for many groups
+// before the first put(), so their loads are in flight together instead of
+// one load-use-store round trip per group.  pre() and put() are kept free of
+// branches but for the store itself: a branch between a load and its use
+// makes the compiler wait for every outstanding memory operation there.
 // ---------------------------------------------------------------------------
 
 // out[m, n] = acc (stored in TO)
@@ -49,9 +51,12 @@ struct EpiStore {
   TO* out;
   int ldo;
   using Row = int64_t;
+  using Col = int;
+  using Key = int;
   static constexpr bool kRowKey = false;
   __device__ __forceinline__ bool vec_ok() const { return (ldo & 3) == 0; }
   __device__ __forceinline__ Row row(int m) const { return static_cast<int64_t>(m) * ldo; }
+  __device__ __forceinline__ Col col(int n) const { return n; }
   __device__ __forceinline__ int row_key(int) const { return 0; }
   __device__ __forceinline__ Row row_from(int m, int) const { return row(m); }
   __device__ __forceinline__ f32x4 pre(Row, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -75,9 +80,12 @@ struct EpiResid {
   const TR* resid;
   int ldo;
   using Row = int64_t;
+  using Col = int;
+  using Key = int;
   static constexpr bool kRowKey = false;
   __device__ __forceinline__ bool vec_ok() const { return (ldo & 3) == 0; }
   __device__ __forceinline__ Row row(int m) const { return static_cast<int64_t>(m) * ldo; }
+  __device__ __forceinline__ Col col(int n) const { return n; }
   __device__ __forceinline__ int row_key(int) const { return 0; }
   __device__ __forceinline__ Row row_from(int m, int) const { return row(m); }
   __device__ __forceinline__ f32x4 pre(Row r, int n) const {
@@ -138,54 +146,58 @@ struct EpiQkv {
     return cs + (static_cast<int64_t>(m) * (hd >> 1) + ((n % hd) >> 1)) * 2;
   }
 
-  // split form (whole groups of four columns inside one head of one segment)
-  struct Row {
-    int64_t m;       // token row
-    int64_t kv_row;  // row of k / v (cache slot row when kv_cap > 0)
-    int pos;         // rotation position
+  // split form (whole groups of four columns inside one head of one segment,
+  // angles from the table).  Everything that depends on the column group is
+  // resolved once in col(), everything that depends on the row once per row
+  // in row_key(), so that pre() and put() are straight-line code: one table
+  // load, the rotation, one store (skipped only for a K/V row with no slot).
+  struct Col {
+    T* base;     // the group's first column in row 0 of its output (q, k or v)
+    int stride;  // elements per output row
+    bool is_q;   // Q: token rows; K / V: the row_key() rows
+    bool rot;    // Q or K: rotate the pairs
+    int pair;    // first rotation pair of the group within its head
   };
+  struct Row {
+    int64_t m;   // token row
+    int64_t kv;  // row of k / v (cache slot row when kv_cap > 0); -1: no slot
+  };
+  using Key = int64_t;
   static constexpr bool kRowKey = true;
   __device__ __forceinline__ bool vec_ok() const {
-    return (hd & 3) == 0 && (nq_hd & 3) == 0 && (nkv_hd & 3) == 0;
+    return cs != nullptr && (hd & 3) == 0 && (nq_hd & 3) == 0 && (nkv_hd & 3) == 0;
   }
-  // the per-token value a row needs from memory (its position), and the row built from it
-  __device__ __forceinline__ int row_key(int m) const { return positions[m]; }
-  __device__ __forceinline__ Row row_from(int m, int pos) const {
-    Row r;
-    r.m = m;
-    r.pos = pos;
-    r.kv_row = kv_cap > 0 ? static_cast<int64_t>(m / seq_len) * kv_cap + pos : static_cast<int64_t>(m);
-    return r;
+  __device__ __forceinline__ Col col(int n) const {
+    Col c;
+    c.is_q = n < nq_hd;
+    const bool is_k = !c.is_q && n < nq_hd + nkv_hd;
+    c.rot = c.is_q || is_k;
+    const int nn = c.is_q ? n : is_k ? n - nq_hd : n - nq_hd - nkv_hd;
+    c.base = (c.is_q ? q : is_k ? k : v) + nn;
+    c.stride = c.is_q ? nq_hd : nkv_hd;
+    c.pair = (n % hd) >> 1;
+    return c;
   }
-  __device__ __forceinline__ Row row(int m) const { return row_from(m, row_key(m)); }
-  // (cos, sin) of the group's two pairs (unused for V columns)
-  __device__ __forceinline__ f32x4 pre(const Row& r, int n) const {
-    if (n >= nq_hd + nkv_hd) return f32x4{1.f, 0.f, 1.f, 0.f};
-    if (cs) return *reinterpret_cast<const f32x4*>(angle(static_cast<int>(r.m), n));
-    const int k = (n % hd) >> 1;
-    float s0, c0, s1, c1;
-    rope_sincos_t<T>(r.pos, rope_inv_freq_pow(rope_base, k), &s0, &c0);
-    rope_sincos_t<T>(r.pos, rope_inv_freq_pow(rope_base, k + 1), &s1, &c1);
-    return f32x4{c0, s0, c1, s1};
+  // the k / v row of token m
+  __device__ __forceinline__ Key row_key(int m) const {
+    if (kv_cap <= 0) return m;
+    const int pos = positions[m];
+    return pos < 0 || pos >= kv_cap ? int64_t{-1} : static_cast<int64_t>(m / seq_len) * kv_cap + pos;
   }
-  __device__ __forceinline__ void put(const Row& r, int n, f32x4 t, const float a[4]) const {
-    if (no_slot(n, r.pos)) return;
-    float o[4] = {a[0], a[1], a[2], a[3]};
-    T* d;
-    if (n < nq_hd) {
-      d = q + r.m * nq_hd + n;
-    } else {
-      const bool is_k = n < nq_hd + nkv_hd;
-      const int nn = is_k ? n - nq_hd : n - nq_hd - nkv_hd;
-      d = (is_k ? k : v) + r.kv_row * nkv_hd + nn;
-    }
-    if (n < nq_hd + nkv_hd) {
-      o[0] = a[0] * t[0] - a[1] * t[1];
-      o[1] = a[0] * t[1] + a[1] * t[0];
-      o[2] = a[2] * t[2] - a[3] * t[3];
-      o[3] = a[2] * t[3] + a[3] * t[2];
-    }
-    Vec4<T>::store(d, o);
+  __device__ __forceinline__ Row row_from(int m, Key kv) const { return Row{m, kv}; }
+  // (cos, sin) of the group's two pairs; identity for V
+  __device__ __forceinline__ f32x4 pre(const Row& r, const Col& c) const {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(cs + (r.m * (hd >> 1) + c.pair) * 2);
+    return c.rot ? t : f32x4{1.f, 0.f, 1.f, 0.f};
+  }
+  __device__ __forceinline__ void put(const Row& r, const Col& c, f32x4 t, const float a[4]) const {
+    float o[4];
+    o[0] = c.rot ? a[0] * t[0] - a[1] * t[1] : a[0];
+    o[1] = c.rot ? a[0] * t[1] + a[1] * t[0] : a[1];
+    o[2] = c.rot ? a[2] * t[2] - a[3] * t[3] : a[2];
+    o[3] = c.rot ? a[2] * t[3] + a[3] * t[2] : a[3];
+    const int64_t row = c.is_q ? r.m : r.kv;
+    if (row >= 0) Vec4<T>::store(c.base + row * c.stride, o);
   }
   __device__ __forceinline__ void operator()(int m, int n, const float v4[4], int cnt) const {
     const int pos = kv_cap > 0 ? positions[m] : 0;
@@ -265,11 +277,14 @@ struct EpiPartial {
   int64_t split_stride;  // elements between consecutive splits
   int half;              // gate/up product: offset of the up columns (= N)
   using Row = int64_t;
+  using Col = int;
+  using Key = int;
   static constexpr bool kRowKey = false;
   __device__ __forceinline__ bool vec_ok() const { return (ldo & 3) == 0; }
   __device__ __forceinline__ Row row(int m) const {
     return blockIdx.z * split_stride + static_cast<int64_t>(m) * ldo;
   }
+  __device__ __forceinline__ Col col(int n) const { return n; }
   __device__ __forceinline__ int row_key(int) const { return 0; }
   __device__ __forceinline__ Row row_from(int m, int) const { return row(m); }
   __device__ __forceinline__ f32x4 pre(Row, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
