@@ -321,13 +321,16 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
     // keeps -inf, and its factor 1 leaves its zero accumulators at zero.)
     {
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      // the factors are all exactly 1 unless some row's maximum moved
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+      }
       m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
     }
 
     const float neg_m = -m_run;
