@@ -310,7 +310,12 @@ attn_flash_kernel(AttnArgs a, int n_qtiles) {
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, cur[h2][e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
+    // lanes l and l ^ 32 hold the two key halves of one query: combine them
+    // with the VALU half swap rather than a round trip through LDS
+    {
+      const auto hv = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(hv[0]), __uint_as_float(hv[1])) * c;
+    }
     // Online softmax: each row's reference m_run is its running maximum
     // (rows whose maximum did not move rescale by exactly exp2(0) = 1).  The
     // weights exp2(score * c - m_run) are rounded to bf16 for the PV product,
