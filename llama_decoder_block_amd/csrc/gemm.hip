@@ -11,7 +11,7 @@
 // gemm_mfma_dma_kernel / gemm_mfma_rs_kernel: prefill (M >= 512, K % 64 == 0,
 //   weight segments on 32-row boundaries).  256x256 tiles, one wavefront per
 //   SIMD owning 128x128, XOR-swizzled LDS; operands loaded straight into LDS
-//   one K step ahead (dma, K <= 8192) or through registers two steps ahead
+//   one K step ahead (dma, K <= 12288) or through registers two steps ahead
 //   (rs, longer K).
 // gemm_skinny_kernel: decode (M <= 64, K % 256 == 0): streams the weights once
 //   with whole-line loads, K split over the wavefronts and summed in LDS.
@@ -87,7 +87,7 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int 
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;
 // longest K (elements) the LDS-DMA prefill kernel takes (see launch_gemm)
-constexpr int kDmaMaxK = 8192;
+constexpr int kDmaMaxK = 12288;
 // compute units of the GPU the large-tile schedule is sized for, and the
 // fewest K steps a split of the large-tile kernels keeps
 constexpr int kCUs = 256;
@@ -1276,8 +1276,10 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
     // Operands straight into LDS for K up to kDmaMaxK; past it the
     // register-staged kernel, whose loads run two K steps ahead instead of
     // one (measured on MI355X: gate/up 1475 against 1519 us, QKV 398
-    // against 412, o equal, but down at K = 14336 863 against 762 us, with
-    // more L2 misses left exposed and a busier texture addresser)
+    // against 412, o equal, the Llama-7B down partials at K = 11008 184-187
+    // against 190-194 us, but down at K = 14336 880 against 752 us, with
+    // more L2 misses left exposed and a busier texture addresser; equal at
+    // K = 22016)
     const bool dma = K <= kDmaMaxK;
     auto go = [&](auto kern, auto e) {
       hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, op, M, N, K, kps, tiles_m, tiles_n, e);
