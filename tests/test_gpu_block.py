@@ -169,6 +169,42 @@ def test_prefill_then_decode(dtype):
     assert torch.count_nonzero(kc[:, T + 1:]) == 0
 
 
+def test_prefill_into_cache_sequence_bounds_inside_tiles():
+    """Three 100-token sequences prefilled into caches at positions 0..99,
+    30..129 and 60..159: the 300 token rows put all three sequences in the
+    first 256-row GEMM tile, with sequence boundaries inside its 32-token
+    blocks, so neighbouring tokens of one block have cache rows in different
+    sequences.  y against both oracles, the written cache slots against the
+    oracle's rotated K and plain V, and the slots no token owns still zero."""
+    B, T, cap = 3, 100, 160
+    wl = small_bf16(batch=B, seq=T, d_ff=1024)
+    inp = synth.make_block_inputs(wl)
+    inp.positions = torch.stack([torch.arange(T, dtype=torch.int32) + off for off in (0, 30, 60)])
+    x, w, pos, _, _ = to_dev(inp)
+    kc = torch.zeros(B, cap, wl.n_kv, wl.head_dim, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    y = binding.block_forward(x, w, pos, wl.n_q, wl.n_kv, wl.theta, wl.eps, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    f = inp.as_f64()
+    z = np.zeros((B, cap, wl.n_kv, wl.head_dim))
+    y_ex, inter = oracle.block_forward(f["x"], f["w"], f["positions"], wl.theta, wl.eps, wl.n_q, wl.n_kv, z, z,
+                                       return_intermediates=True)
+    y_st = oracle.block_forward(f["x"], f["w"], f["positions"], wl.theta, wl.eps, wl.n_q, wl.n_kv, z, z,
+                                bf16_storage=True)
+    report("prefill into cache, 3 x 100 tokens", y, y_ex)
+    x64 = to64(inp.x)
+    assert rel_frobenius(y, y_ex) <= 1e-2
+    assert max_abs(y, y_st) <= 5e-2
+    assert rel_frobenius(to64(y) - x64, y_ex - x64) <= 1e-2
+    written = np.zeros((B, cap), dtype=bool)
+    for b in range(B):
+        written[b, inp.positions[b].numpy()] = True
+    for got, want in ((kc, inter["k_cache"]), (vc, inter["v_cache"])):
+        g = to64(got.cpu())
+        assert rel_frobenius(g[written], want[written]) <= 1e-2
+        assert not np.any(g[~written])
+
+
 def test_decode_workload_sampled():
     """Full-size decode workload (64 sequences, cache of 4096 + 1 slots):
     all 64 outputs from the GPU, 8 sequences checked against the oracle."""
