@@ -1159,12 +1159,16 @@ BufOperands buf_operands(const bf16_t* x, const WSeg& w, int N, bool dual) {
 // 256 and weight segments starting on 32-row boundaries.
 bool skinny_shape(DType dt, int M, int K) { return dt == DType::BF16 && M <= 64 && K % 256 == 0; }
 
-// K splits across workgroups: until there are >= 384 workgroups (1.5 per
-// CU), keeping K / splits a multiple of 256.
-int skinny_splits(int n_logical, int K) {
+// K splits across workgroups, keeping K / splits a multiple of 256: with
+// more than 32 token rows until there are >= 192 workgroups, with fewer until
+// there are >= 384 (measured on the Llama-3-8B decode step: 64 rows, O and
+// down at 4 splits instead of 8 and QKV at 2 instead of 4, step 334.5 ->
+// 327.0-328.5 us; 8 rows, the same splits cost 3 us per step)
+int skinny_splits(int n_logical, int K, int M) {
   const int nb = ceil_div(n_logical, 64);
+  const int target = M > 32 ? 192 : 384;
   int splits = 1;
-  while (nb * splits < 384 && K % (splits * 2 * 256) == 0) splits *= 2;
+  while (nb * splits < target && K % (splits * 2 * 256) == 0) splits *= 2;
   return splits;
 }
 
@@ -1176,7 +1180,7 @@ size_t gemm_workspace_bytes(DType dt, int M, int N, int K, bool dual) {
   size_t need = 0;
   if (p.mfma && p.splits > 1) need = static_cast<size_t>(p.splits) * M * n_logical * sizeof(float);
   if (skinny_shape(dt, M, K)) {
-    const int sk = skinny_splits(n_logical, K);
+    const int sk = skinny_splits(n_logical, K, M);
     if (sk > 1) need = std::max(need, static_cast<size_t>(sk) * M * n_logical * sizeof(float));
   }
   return need;
@@ -1224,7 +1228,7 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
   auto rows = make_rows<bf16_t>(W, K);
   if (skinny_shape(dt, M, K) && rs_ok(W, K)) {
     const int n_logical = dual ? 2 * N : N;
-    const int splits = skinny_splits(n_logical, K);
+    const int splits = skinny_splits(n_logical, K, M);
     const int ks = K / splits;
     if (splits == 1) {
       if (kernel_name) *kernel_name = dual ? "gemm_skinny_gate_up_silu" : "gemm_skinny";
