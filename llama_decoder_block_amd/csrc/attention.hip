@@ -1162,6 +1162,12 @@ constexpr int kDecWavesPerCu = 6;
 // in flight; its sweep on the same workload: 4 / 6 / 8 / 10 / 12 / 16 per CU
 // gave 131 / 115 / 109 / 121 / 119 / 120 us.
 constexpr int kDecWavesPerCuFp8 = 8;
+// The split path (few pairs, long histories) sizes its chunks for one
+// four-wavefront workgroup per CU: on MI355X, 8 sequences x 8 KV heads at
+// 32768 slots took 288 / 209 / 190 / 240 / 210 / 207 / 211 us with chunks for
+// 2 / 3 / 4 / 5 / 6 / 8 / 12 wavefronts per CU (fewer than one workgroup per
+// CU leaves CUs idle, a fraction more leaves a tail).
+constexpr int kDecSplitWavesPerCu = 4;
 
 // Wavefronts per (sequence, KV head) workgroup of attn_decode3_kernel: close
 // to the target count, all workgroups resident in one round, within LDS.
@@ -1196,7 +1202,7 @@ hipError_t launch_decode_bf16(const AttnArgs& a, void* ws, hipStream_t s, const 
   // into chunks across wavefronts of their own, then merge the partials
   if (kernel_name)
     *kernel_name = KV8 ? "attn_decode_splitk_fp8kv" : PAGED ? "attn_decode_splitk_paged" : "attn_decode_splitk";
-  const int64_t want = std::max<int64_t>(1, target / pairs);
+  const int64_t want = std::max<int64_t>(1, static_cast<int64_t>(device_cus()) * kDecSplitWavesPerCu / pairs);
   int chunk = static_cast<int>(((a.S + want - 1) / want + kDSub - 1) / kDSub * kDSub);
   chunk = std::max(chunk, kDChunk);  // never more chunks than the workspace holds
   const int nch = (a.S + chunk - 1) / chunk;
