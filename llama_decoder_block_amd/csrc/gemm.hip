@@ -979,18 +979,27 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
           acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fb], b[tb], acc[fb][tb], 0, 0, 0);
     }
   };
-  // The next step's loads are in flight while this step multiplies out of
-  // LDS.  LDS accesses of one wavefront execute in order, so a step's stores
-  // may follow the previous step's fragment reads without a barrier.  The
-  // load past the last step re-reads it (cache hits).
-  Stage g;
-  gload(g, 0);
-  lstore(g);
-  for (int st = 0; st < nsteps; ++st) {
-    gload(g, st + 1);
+  // Two register stages: the loads of the next two steps are in flight
+  // while a step multiplies out of LDS (the wavefronts of a short product
+  // have only a few steps each, so one step of lookahead leaves most of the
+  // load latency exposed).  LDS accesses of one wavefront execute in order,
+  // so a step's stores may follow the previous step's fragment reads without
+  // a barrier.  Loads past the last step re-read it (cache hits).
+  Stage g0, g1;
+  gload(g0, 0);
+  gload(g1, 1);
+  lstore(g0);
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    // LDS holds step st, g1 step st + 1
+    gload(g0, st + 2);
     compute();
-    lstore(g);
+    lstore(g1);
+    gload(g1, st + 3);
+    compute();
+    lstore(g0);
   }
+  if (st < nsteps) compute();  // an odd step count's last step
 
   // sum the four wavefronts' tiles: C register e is row (e/4)*8 + fh*4 + e%4
   // of a 32-row block and token fr of a 32-token block.  The sum buffer is
