@@ -77,7 +77,11 @@ rmsnorm_vec_kernel(const TR* __restrict__ x, const TR* __restrict__ res,
 // four (a wavefront load covers 256 contiguous elements), so every lane has V
 // loads in flight at once and the sum of squares needs only the wavefront's
 // own butterfly, no LDS and no barrier.
-template <typename TR, typename TO, int V>
+// EARLY_G: gamma is loaded with the row rather than after the reduction, one
+// memory round trip per row instead of two (what sets the time of a few rows,
+// as in decode), at the cost of the registers that hold it (occupancy, what
+// sets the time of many rows).
+template <typename TR, typename TO, int V, bool EARLY_G>
 __global__ void __launch_bounds__(kNormThreads)
 rmsnorm_wave_kernel(const TR* __restrict__ x, const TR* __restrict__ res,
                     const TO* __restrict__ gamma, TO* __restrict__ out, TR* sum_out,
@@ -87,9 +91,14 @@ rmsnorm_wave_kernel(const TR* __restrict__ x, const TR* __restrict__ res,
   if (row >= rows) return;
   const int64_t base = row * d;
   float v[V][4];
+  float gm[EARLY_G ? V : 1][4];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < V; ++c) Vec4<TR>::load(x + base + 4 * (lane + 64 * c), v[c]);
+  if constexpr (EARLY_G) {
+#pragma unroll
+    for (int c = 0; c < V; ++c) Vec4<TO>::load(gamma + 4 * (lane + 64 * c), gm[c]);
+  }
   if (res) {
 #pragma unroll
     for (int c = 0; c < V; ++c) {
@@ -109,7 +118,12 @@ rmsnorm_wave_kernel(const TR* __restrict__ x, const TR* __restrict__ res,
 #pragma unroll
   for (int c = 0; c < V; ++c) {
     float g[4], o[4];
-    Vec4<TO>::load(gamma + 4 * (lane + 64 * c), g);
+    if constexpr (EARLY_G) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[e] = gm[c][e];
+    } else {
+      Vec4<TO>::load(gamma + 4 * (lane + 64 * c), g);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = v[c][e] * inv * g[e];
     Vec4<TO>::store(out + base + 4 * (lane + 64 * c), o);
@@ -153,9 +167,14 @@ hipError_t launch_rmsnorm_t(const void* x, const void* res, const void* gamma, v
   const int per_lane = d % 256 == 0 ? d / 256 : 0;  // 4-element chunks per lane on the wavefront path
   if (per_lane == 1 || per_lane == 2 || per_lane == 4 || per_lane == 8 || per_lane == 16 || per_lane == 32) {
     const dim3 wgrid(static_cast<unsigned>((rows + 3) / 4));
+    // fewer row workgroups than CUs: latency-bound, gamma with the row
+    const bool early = (rows + 3) / 4 < 256;
     auto go = [&](auto vc) {
       constexpr int V = decltype(vc)::value;
-      hipLaunchKernelGGL((rmsnorm_wave_kernel<TR, TO, V>), wgrid, block, 0, s, xp, rp, gp, op, sp, rows, d, eps);
+      if (early)
+        hipLaunchKernelGGL((rmsnorm_wave_kernel<TR, TO, V, true>), wgrid, block, 0, s, xp, rp, gp, op, sp, rows, d, eps);
+      else
+        hipLaunchKernelGGL((rmsnorm_wave_kernel<TR, TO, V, false>), wgrid, block, 0, s, xp, rp, gp, op, sp, rows, d, eps);
     };
     switch (per_lane) {
       case 1: go(std::integral_constant<int, 1>{}); break;
