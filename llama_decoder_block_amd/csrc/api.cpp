@@ -497,18 +497,23 @@ int run_block(const void* x, void* y, const llama_block_weights* w, const int32_
     wo.ptr[0] = w->wo; wo.start[0] = 0; wo.start[1] = d; wo.nseg = 1;
     lb::GemmEpi ep{};
     ep.kind = lb::EpiKind::Resid; ep.out_dt = rdt; ep.out = h_buf; ep.resid = x; ep.ldo = d;
+    // few rows: the residual add joins the FFN pre-norm in one pass over
+    // the split-K partials (this leg then leaves only the partials)
+    const bool fused = lb::resid_norm_fused(wdt, rdt, M, nq * hd, wo, d);
     e = timed("o_resid", s, [&](const char** name) {
-      return lb::launch_gemm(wdt, o_buf, M, nq * hd, wo, d, false, ep, gemm_ws, p.gemm, s, name);
+      return fused ? lb::launch_gemm_partials(wdt, o_buf, M, nq * hd, wo, d, gemm_ws, p.gemm, s, name)
+                   : lb::launch_gemm(wdt, o_buf, M, nq * hd, wo, d, false, ep, gemm_ws, p.gemm, s, name);
     });
     if (e != hipSuccess) return hip_fail(e, "block forward: o projection");
-  }
 
-  // a8: FFN pre-norm (f reuses the a buffer)
-  e = timed("ffn_norm", s, [&](const char** name) {
-    *name = "rmsnorm";
-    return lb::launch_rmsnorm(h_buf, nullptr, w->ffn_norm, a_buf, nullptr, M, d, feps, wdt, rdt, s);
-  });
-  if (e != hipSuccess) return hip_fail(e, "block forward: ffn norm");
+    // a8: FFN pre-norm (f reuses the a buffer)
+    e = timed("ffn_norm", s, [&](const char** name) {
+      if (fused) return lb::launch_resid_norm(M, nq * hd, d, gemm_ws, x, h_buf, w->ffn_norm, a_buf, feps, s, name);
+      *name = "rmsnorm";
+      return lb::launch_rmsnorm(h_buf, nullptr, w->ffn_norm, a_buf, nullptr, M, d, feps, wdt, rdt, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "block forward: ffn norm");
+  }
 
   // a9/a10: SwiGLU FFN + residual into y
   e = run_ffn(a_buf, w->w_gate, w->w_up, w->w_down, h_buf, y, M, d, d_ff, wdt, rdt, mact, gemm_ws, p.gemm, s);

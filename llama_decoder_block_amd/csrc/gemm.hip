@@ -878,6 +878,87 @@ splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t split_s
 }
 
 // ---------------------------------------------------------------------------
+// split-K reduction + residual + the RMSNorm of the result, one workgroup per
+// token row (few rows: the decode step's O projection followed by the FFN
+// pre-norm, "LLaMA Architecture" block structure: h = x + attention output,
+// then RMSNorm(h) feeds the FFN).  h = resid + sum of the fp32 partials, the
+// splits added in order as splitk_reduce_kernel adds them (h is bit-identical
+// to that kernel's with the residual epilogue); then, with the row held in
+// registers, f = h * (mean(h^2) + eps)^-1/2 * gamma as the RMSNorm kernels
+// compute it (sum of squares per lane, then over the wavefront, then over the
+// four wavefronts in order).  Wavefront w covers columns [w d/4, (w+1) d/4),
+// lane l the four columns w d/4 + 4 (l + 64 c), c < V = d / 1024.  One
+// memory round trip per row for all loads (partials, residual, gamma) instead
+// of two kernels with one each.
+// ---------------------------------------------------------------------------
+template <int V>
+__global__ void __launch_bounds__(256)
+splitk_resid_norm_kernel(const float* __restrict__ part, int splits, int64_t split_stride, int d,
+                         const float* __restrict__ resid, float* __restrict__ h, const bf16_t* __restrict__ gamma,
+                         bf16_t* __restrict__ f, float eps) {
+  __shared__ float red[4];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * d;
+  const int c0 = wid * (d >> 2);
+  float a[V][4], r[V][4], g[V][4];
+#pragma unroll
+  for (int c = 0; c < V; ++c) {
+    const int n = c0 + 4 * (lane + 64 * c);
+    Vec4<float>::load(resid + row + n, r[c]);
+    Vec4<bf16_t>::load(gamma + n, g[c]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[c][e] = 0.f;
+  }
+  // four splits' loads in flight at once, added in split order
+  const float* pr = part + row + c0 + 4 * lane;
+  int z = 0;
+  for (; z + 4 <= splits; z += 4) {
+    float t[4][V][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < V; ++c) Vec4<float>::load(pr + (z + i) * split_stride + 256 * c, t[i][c]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < V; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[c][e] += t[i][c][e];
+  }
+  for (; z < splits; ++z) {
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+      float t[4];
+      Vec4<float>::load(pr + z * split_stride + 256 * c, t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[c][e] += t[e];
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < V; ++c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[c][e] = r[c][e] + a[c][e];
+      ss += a[c][e] * a[c][e];
+    }
+    Vec4<float>::store(h + row + c0 + 4 * (lane + 64 * c), a[c]);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wid] = ss;
+  __syncthreads();
+  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+  const float inv = rsqrtf(tot / static_cast<float>(d) + eps);
+#pragma unroll
+  for (int c = 0; c < V; ++c) {
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = a[c][e] * inv * g[c][e];
+    Vec4<bf16_t>::store(f + row + c0 + 4 * (lane + 64 * c), o);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Skinny MFMA kernel for few token rows (decode: M <= 64).  The product is
 // bound by streaming the weights once, so the kernel is built around that
 // stream: a workgroup owns 64 weight rows (for the fused gate/up product 32
@@ -1376,6 +1457,55 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
                        part, p.splits, split_stride, M, N, n_logical, e);
     return hipGetLastError();
   });
+}
+
+
+bool resid_norm_fused(DType dt, DType rdt, int M, int K, const WSeg& W, int N) {
+  if (M <= 0 || rdt != DType::F32 || !skinny_shape(dt, M, K) || !rs_ok(W, K)) return false;
+  if (N % 1024 != 0) return false;
+  const int v = N / 1024;
+  if (v != 1 && v != 2 && v != 4 && v != 8) return false;
+  return skinny_splits(N, K, M) > 1;
+}
+
+hipError_t launch_gemm_partials(DType dt, const void* X, int M, int K, const WSeg& W, int N, void* ws,
+                                size_t ws_bytes, hipStream_t s, const char** kernel_name) {
+  if (!resid_norm_fused(dt, DType::F32, M, K, W, N)) return hipErrorInvalidValue;
+  const int splits = skinny_splits(N, K, M);
+  const size_t need = static_cast<size_t>(splits) * M * N * sizeof(float);
+  if (ws == nullptr || ws_bytes < need) return hipErrorInvalidValue;
+  if (kernel_name) *kernel_name = "gemm_skinny_splitk";
+  const bf16_t* xp = static_cast<const bf16_t*>(X);
+  EpiPartial pe{static_cast<float*>(ws), N, static_cast<int64_t>(M) * N};
+  BufOperands op = buf_operands(xp, W, N, false);
+  hipLaunchKernelGGL((gemm_skinny_kernel<false, EpiPartial>), dim3(ceil_div(N, 64), 1, splits), dim3(256), 0, s,
+                     xp, op, M, N, K, K / splits, pe);
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_norm(int M, int K, int N, const void* ws, const void* resid, void* h, const void* gamma,
+                             void* f, float eps, hipStream_t s, const char** kernel_name) {
+  if (M <= 0) return hipSuccess;
+  if (N % 1024 != 0 || N > 8192 || K % 256 != 0) return hipErrorInvalidValue;
+  const int splits = skinny_splits(N, K, M);
+  if (kernel_name) *kernel_name = "splitk_resid_norm";
+  const float* part = static_cast<const float*>(ws);
+  const int64_t stride = static_cast<int64_t>(M) * N;
+  const float* r = static_cast<const float*>(resid);
+  float* hp = static_cast<float*>(h);
+  const bf16_t* g = static_cast<const bf16_t*>(gamma);
+  bf16_t* fp = static_cast<bf16_t*>(f);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(M), dim3(256), 0, s, part, splits, stride, N, r, hp, g, fp, eps);
+    return hipGetLastError();
+  };
+  switch (N / 1024) {
+    case 1: return go(splitk_resid_norm_kernel<1>);
+    case 2: return go(splitk_resid_norm_kernel<2>);
+    case 4: return go(splitk_resid_norm_kernel<4>);
+    case 8: return go(splitk_resid_norm_kernel<8>);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace lb

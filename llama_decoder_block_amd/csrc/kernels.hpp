@@ -332,6 +332,21 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
                        const GemmEpi& epi, void* ws, size_t ws_bytes, hipStream_t s,
                        const char** kernel_name);
 
+// Few token rows (the skinny split-K path), a residual epilogue and an
+// RMSNorm of its result, as in the decode step's O projection and FFN
+// pre-norm: the GEMM leaves fp32 partials in ws (launch_gemm_partials), and
+// launch_resid_norm sums them with the residual into h (fp32, bit-identical to
+// launch_gemm's residual epilogue) and writes f = RMSNorm(h) * gamma (bf16).
+// resid_norm_fused says whether a shape takes this path (bf16 operands, fp32
+// residual, N a multiple of 1024 up to 8192, a K split); otherwise the caller
+// runs launch_gemm and launch_rmsnorm.  ws needs gemm_workspace_bytes(dt, M,
+// N, K, false) bytes and must not be touched between the two calls.
+bool resid_norm_fused(DType dt, DType rdt, int M, int K, const WSeg& W, int N);
+hipError_t launch_gemm_partials(DType dt, const void* X, int M, int K, const WSeg& W, int N, void* ws,
+                                size_t ws_bytes, hipStream_t s, const char** kernel_name);
+hipError_t launch_resid_norm(int M, int K, int N, const void* ws, const void* resid, void* h, const void* gamma,
+                             void* f, float eps, hipStream_t s, const char** kernel_name);
+
 // ---------------------------------------------------------------------------
 // Other launchers
 // ---------------------------------------------------------------------------

@@ -234,6 +234,19 @@ def test_decode_workload_sampled():
     assert torch.count_nonzero(kc[:, 4096]) > 0
 
 
+@pytest.mark.parametrize("d,n_q,n_kv,batch", [(1024, 8, 2, 64), (2048, 16, 4, 33), (8192, 64, 8, 3)])
+def test_decode_residual_norm_pass(d, n_q, n_kv, batch):
+    """Decode rows at model widths that are multiples of 1024 (1, 2 and 8
+    column chunks per lane): the O projection leaves split-K partials and one
+    pass per row adds them to the residual and applies the FFN pre-norm.  The
+    block output and h against both oracles, every row."""
+    wl = synth.workload("llama3_8b_gqa_decode", batch=batch, d_model=d, n_q=n_q, n_kv=n_kv, head_dim=128,
+                        d_ff=1536, decode_pos=70, kv_cap=96)
+    inp = synth.make_block_inputs(wl)
+    y, _, _ = run_block(inp)
+    check_bf16(f"decode d={d} B={batch}", y, inp)
+
+
 def test_prefill_workload_sampled_rows():
     """Full Llama-3-8B prefill (T = 8192): sampled rows against the oracle."""
     wl = synth.workload("llama3_8b_gqa_prefill")
