@@ -881,9 +881,9 @@ splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t split_s
 // split-K reduction + residual + the RMSNorm of the result, one workgroup per
 // token row (few rows: the decode step's O projection followed by the FFN
 // pre-norm, "LLaMA Architecture" block structure: h = x + attention output,
-// then RMSNorm(h) feeds the FFN).  h = resid + sum of the fp32 partials, the
-// splits added in order as splitk_reduce_kernel adds them (h is bit-identical
-// to that kernel's with the residual epilogue); then, with the row held in
+// then RMSNorm(h) feeds the FFN).  h = resid + sum of the fp32 partials, with
+// the additions of splitk_reduce_kernel and its residual epilogue in the same
+// order (splits in turn from zero, then the residual); then, with the row held in
 // registers, f = h * (mean(h^2) + eps)^-1/2 * gamma as the RMSNorm kernels
 // compute it (sum of squares per lane, then over the wavefront, then over the
 // four wavefronts in order).  Wavefront w covers columns [w d/4, (w+1) d/4),

@@ -335,8 +335,9 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
 // Few token rows (the skinny split-K path), a residual epilogue and an
 // RMSNorm of its result, as in the decode step's O projection and FFN
 // pre-norm: the GEMM leaves fp32 partials in ws (launch_gemm_partials), and
-// launch_resid_norm sums them with the residual into h (fp32, bit-identical to
-// launch_gemm's residual epilogue) and writes f = RMSNorm(h) * gamma (bf16).
+// launch_resid_norm sums them with the residual into h (fp32, the additions of
+// launch_gemm's residual epilogue in the same order) and writes
+// f = RMSNorm(h) * gamma (bf16).
 // resid_norm_fused says whether a shape takes this path (bf16 operands, fp32
 // residual, N a multiple of 1024 up to 8192, a K split); otherwise the caller
 // runs launch_gemm and launch_rmsnorm.  ws needs gemm_workspace_bytes(dt, M,
