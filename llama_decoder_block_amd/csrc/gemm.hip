@@ -889,12 +889,13 @@ splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t split_s
 // four wavefronts in order).  Wavefront w covers columns [w d/4, (w+1) d/4),
 // lane l the four columns w d/4 + 4 (l + 64 c), c < V = d / 1024.  One
 // memory round trip per row for all loads (partials, residual, gamma) instead
-// of two kernels with one each.
+// of two kernels with one each.  h may be resid itself (each lane reads its
+// residual elements before it writes them).
 // ---------------------------------------------------------------------------
 template <int V>
 __global__ void __launch_bounds__(256)
 splitk_resid_norm_kernel(const float* __restrict__ part, int splits, int64_t split_stride, int d,
-                         const float* __restrict__ resid, float* __restrict__ h, const bf16_t* __restrict__ gamma,
+                         const float* resid, float* h, const bf16_t* __restrict__ gamma,
                          bf16_t* __restrict__ f, float eps) {
   __shared__ float red[4];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -1458,7 +1459,6 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
     return hipGetLastError();
   });
 }
-
 
 bool resid_norm_fused(DType dt, DType rdt, int M, int K, const WSeg& W, int N) {
   if (M <= 0 || rdt != DType::F32 || !skinny_shape(dt, M, K) || !rs_ok(W, K)) return false;

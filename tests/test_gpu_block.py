@@ -234,7 +234,7 @@ def test_decode_workload_sampled():
     assert torch.count_nonzero(kc[:, 4096]) > 0
 
 
-@pytest.mark.parametrize("d,n_q,n_kv,batch", [(1024, 8, 2, 64), (2048, 16, 4, 33), (8192, 64, 8, 3)])
+@pytest.mark.parametrize("d,n_q,n_kv,batch", [(1024, 8, 2, 64), (1024, 8, 2, 1), (2048, 16, 4, 33), (8192, 64, 8, 3)])
 def test_decode_residual_norm_pass(d, n_q, n_kv, batch):
     """Decode rows at model widths that are multiples of 1024 (1, 2 and 8
     column chunks per lane): the O projection leaves split-K partials and one
