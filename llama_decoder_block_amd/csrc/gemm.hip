@@ -14,7 +14,9 @@
 //   one K step ahead (dma, K <= 12288) or through registers two steps ahead
 //   (rs, longer K).
 // gemm_skinny_kernel: decode (M <= 64, K % 256 == 0): streams the weights once
-//   with whole-line loads, K split over the wavefronts and summed in LDS.
+//   with whole-line loads, K split over the wavefronts and summed in LDS;
+//   64 or 32 weight rows per workgroup, K also split over workgroups (fp32
+//   partials + splitk_reduce_kernel) when the row blocks cannot fill the GPU.
 // gemm_mfma_kernel: generic tiles (64x64 .. 256x256) for every other bf16
 //   shape; with few rows it writes fp32 partial sums per K slice and
 //   splitk_reduce_kernel sums them and applies the epilogue.
@@ -978,9 +980,14 @@ constexpr int kSkStep = 64;  // K elements per step
 
 __device__ __forceinline__ int sk_idx(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
-template <bool DUAL, class Epi>
+// FB: 32-row weight blocks per workgroup (2, or 1 for a product with too few
+// row blocks of 64 to fill the GPU without a K split; the fused gate/up
+// product always takes one gate and one up block).
+template <bool DUAL, int FB, class Epi>
 __global__ void __launch_bounds__(256, 2)
 gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, int K, int ks, Epi epi) {
+  static_assert(FB == 2 || (FB == 1 && !DUAL), "one or two 32-row weight blocks");
+  constexpr int WROWS = 32 * FB;  // weight rows of the workgroup
   // per wavefront: 64 weight rows + 64 token rows of one step (128 B each);
   // reused afterwards for the cross-wavefront sum
   __shared__ u32x4 lds[4][2][64 * 8];
@@ -991,9 +998,9 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
   const uint32_t row_bytes = static_cast<uint32_t>(K) * 2u;
 
   // buffer resources of the two 32-row weight blocks of this workgroup
-  __amdgpu_buffer_rsrc_t wr[2];
+  __amdgpu_buffer_rsrc_t wr[FB];
 #pragma unroll
-  for (int fb = 0; fb < 2; ++fb) {
+  for (int fb = 0; fb < FB; ++fb) {
     const bf16_t* base;
     int left;
     if (DUAL) {
@@ -1001,7 +1008,7 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
       base = op.w[fb] + static_cast<int64_t>(f0) * K;
       left = op.wrows[fb] - f0;
     } else {
-      const int r0 = blockIdx.x * 64 + fb * 32;
+      const int r0 = blockIdx.x * WROWS + fb * 32;
       const int seg = r0 < op.s1 ? 0 : r0 < op.s2 ? 1 : 2;
       const int start = seg == 0 ? 0 : seg == 1 ? op.s1 : op.s2;
       base = op.w[seg] + static_cast<int64_t>(r0 - start) * K;
@@ -1021,12 +1028,12 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
   const int lrow = lane >> 3, lchunk = lane & 7;
   const uint32_t voff = static_cast<uint32_t>(lrow) * row_bytes + lchunk * 16u;
   struct Stage {
-    u32x4 w[8], x[8];
+    u32x4 w[4 * FB], x[8];
   };
   auto gload = [&](Stage& g, int step) {
     const uint32_t soff = static_cast<uint32_t>(k0 + min(step, nsteps - 1) * kSkStep) * 2u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) g.w[i] = buffer_load16(wr[i >> 2], voff + static_cast<uint32_t>(i & 3) * 8u * row_bytes, soff);
+    for (int i = 0; i < 4 * FB; ++i) g.w[i] = buffer_load16(wr[i >> 2], voff + static_cast<uint32_t>(i & 3) * 8u * row_bytes, soff);
 #pragma unroll
     for (int i = 0; i < 8; ++i) g.x[i] = buffer_load16(xr, voff + static_cast<uint32_t>(i) * 8u * row_bytes, soff);
   };
@@ -1034,13 +1041,13 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
   u32x4* lx = lds[w][1];
   auto lstore = [&](const Stage& g) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lw[sk_idx(i * 8 + lrow, lchunk)] = g.w[i];
+    for (int i = 0; i < 4 * FB; ++i) lw[sk_idx(i * 8 + lrow, lchunk)] = g.w[i];
 #pragma unroll
     for (int i = 0; i < 8; ++i) lx[sk_idx(i * 8 + lrow, lchunk)] = g.x[i];
   };
-  f32x16 acc[2][2];
+  f32x16 acc[FB][2];
 #pragma unroll
-  for (int fb = 0; fb < 2; ++fb)
+  for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -1049,13 +1056,13 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
   auto compute = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      bf16x8 a[2], b[2];
+      bf16x8 a[FB], b[2];
 #pragma unroll
-      for (int fb = 0; fb < 2; ++fb) a[fb] = __builtin_bit_cast(bf16x8, lw[sk_idx(fb * 32 + fr, 2 * i + fh)]);
+      for (int fb = 0; fb < FB; ++fb) a[fb] = __builtin_bit_cast(bf16x8, lw[sk_idx(fb * 32 + fr, 2 * i + fh)]);
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) b[tb] = __builtin_bit_cast(bf16x8, lx[sk_idx(tb * 32 + fr, 2 * i + fh)]);
 #pragma unroll
-      for (int fb = 0; fb < 2; ++fb)
+      for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
           acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fb], b[tb], acc[fb][tb], 0, 0, 0);
@@ -1090,7 +1097,7 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
   f32x4* red = reinterpret_cast<f32x4*>(&lds[0][0][0]);
   auto rix = [](int wv, int tok, int chunk) { return (wv * 64 + tok) * 16 + (chunk ^ (tok & 15)); };
 #pragma unroll
-  for (int fb = 0; fb < 2; ++fb)
+  for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -1118,10 +1125,11 @@ gemm_skinny_kernel(const bf16_t* __restrict__ X, BufOperands op, int M, int N, i
       epi(m, c, gv, uv, min(4, N - c));
     }
   } else {
+    // thread (m, q): rows q * WROWS / 4 + 4 g of the workgroup's block
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int row = q * 16 + g * 4;
-      const int n = blockIdx.x * 64 + row;
+    for (int g = 0; g < FB * 2; ++g) {
+      const int row = q * (WROWS / 4) + g * 4;
+      const int n = blockIdx.x * WROWS + row;
       if (n >= N) continue;
       const f32x4 v4 = sum4(row);
       const float v[4] = {v4[0], v4[1], v4[2], v4[3]};
@@ -1255,9 +1263,10 @@ bool skinny_shape(DType dt, int M, int K) { return dt == DType::BF16 && M <= 64 
 // there are >= 384 (measured on the Llama-3-8B decode step: 64 rows, O and
 // down at 4 splits instead of 8 and QKV at 2 instead of 4, step 334.5 ->
 // 327.0-328.5 us; 8 rows, the same splits cost 3 us per step)
+int skinny_target(int M) { return M > 32 ? 192 : 384; }
 int skinny_splits(int n_logical, int K, int M) {
   const int nb = ceil_div(n_logical, 64);
-  const int target = M > 32 ? 192 : 384;
+  const int target = skinny_target(M);
   int splits = 1;
   while (nb * splits < target && K % (splits * 2 * 256) == 0) splits *= 2;
   return splits;
@@ -1321,17 +1330,29 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
     const int n_logical = dual ? 2 * N : N;
     const int splits = skinny_splits(n_logical, K, M);
     const int ks = K / splits;
+    if (!dual && splits > 1 && ceil_div(N, 32) >= skinny_target(M)) {
+      // enough 32-row weight blocks to fill the GPU: no K split, so the
+      // epilogue (e.g. the rotation and cache append of QKV) runs here and
+      // no partials go through HBM (Llama-3-8B decode QKV: 192 workgroups)
+      if (kernel_name) *kernel_name = "gemm_skinny_narrow";
+      BufOperands op = buf_operands(xp, W, N, false);
+      return with_epi(epi, [&](auto e) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<false, 1, decltype(e)>), dim3(ceil_div(N, 32)), dim3(256), 0, s, xp,
+                           op, M, N, K, K, e);
+        return hipGetLastError();
+      });
+    }
     if (splits == 1) {
       if (kernel_name) *kernel_name = dual ? "gemm_skinny_gate_up_silu" : "gemm_skinny";
       BufOperands op = buf_operands(xp, W, N, dual);
       dim3 grid(ceil_div(n_logical, 64), 1, 1);
       if (dual)
         return with_silu(epi, [&](auto e) {
-          hipLaunchKernelGGL((gemm_skinny_kernel<true, decltype(e)>), grid, dim3(256), 0, s, xp, op, M, N, K, ks, e);
+          hipLaunchKernelGGL((gemm_skinny_kernel<true, 2, decltype(e)>), grid, dim3(256), 0, s, xp, op, M, N, K, ks, e);
           return hipGetLastError();
         });
       return with_epi(epi, [&](auto e) {
-        hipLaunchKernelGGL((gemm_skinny_kernel<false, decltype(e)>), grid, dim3(256), 0, s, xp, op, M, N, K, ks, e);
+        hipLaunchKernelGGL((gemm_skinny_kernel<false, 2, decltype(e)>), grid, dim3(256), 0, s, xp, op, M, N, K, ks, e);
         return hipGetLastError();
       });
     }
@@ -1343,7 +1364,7 @@ hipError_t launch_gemm(DType dt, const void* X, int M, int K, const WSeg& W, int
     const int64_t split_stride = static_cast<int64_t>(M) * n_logical;
     EpiPartial pe{part, n_logical, split_stride};
     BufOperands op = buf_operands(xp, W, n_logical, false);
-    hipLaunchKernelGGL((gemm_skinny_kernel<false, EpiPartial>), dim3(ceil_div(n_logical, 64), 1, splits), dim3(256),
+    hipLaunchKernelGGL((gemm_skinny_kernel<false, 2, EpiPartial>), dim3(ceil_div(n_logical, 64), 1, splits), dim3(256),
                        0, s, xp, op, M, n_logical, K, ks, pe);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -1478,7 +1499,7 @@ hipError_t launch_gemm_partials(DType dt, const void* X, int M, int K, const WSe
   const bf16_t* xp = static_cast<const bf16_t*>(X);
   EpiPartial pe{static_cast<float*>(ws), N, static_cast<int64_t>(M) * N};
   BufOperands op = buf_operands(xp, W, N, false);
-  hipLaunchKernelGGL((gemm_skinny_kernel<false, EpiPartial>), dim3(ceil_div(N, 64), 1, splits), dim3(256), 0, s,
+  hipLaunchKernelGGL((gemm_skinny_kernel<false, 2, EpiPartial>), dim3(ceil_div(N, 64), 1, splits), dim3(256), 0, s,
                      xp, op, M, N, K, K / splits, pe);
   return hipGetLastError();
 }

@@ -247,6 +247,23 @@ def test_decode_residual_norm_pass(d, n_q, n_kv, batch):
     check_bf16(f"decode d={d} B={batch}", y, inp)
 
 
+def test_decode_qkv_without_k_split():
+    """40 decode rows whose Q/K/V product has too few 64-row weight blocks to
+    fill the GPU but enough 32-row ones (8192 rows: 256 workgroups): the
+    product runs unsplit on 32-row blocks, with the rotation and the cache
+    append in its own epilogue.  Block output and h against both oracles,
+    every row, and the appended cache slot against the oracle's."""
+    wl = synth.workload("llama3_8b_gqa_decode", batch=40, d_model=6144, n_q=48, n_kv=8, head_dim=128,
+                        d_ff=1536, decode_pos=70, kv_cap=96)
+    inp = synth.make_block_inputs(wl)
+    y, kc, _ = run_block(inp)
+    check_bf16("decode QKV on 32-row blocks", y, inp)
+    _, inter = oracle_block(inp)
+    new_k = to64(kc[:, 70])
+    assert rel_frobenius(new_k, inter["k_cache"][:, 70]) <= 1e-2
+    assert torch.equal(kc[:, 71:].cpu(), inp.k_cache[:, 71:])
+
+
 def test_prefill_workload_sampled_rows():
     """Full Llama-3-8B prefill (T = 8192): sampled rows against the oracle."""
     wl = synth.workload("llama3_8b_gqa_prefill")
