@@ -696,16 +696,16 @@ __device__ __forceinline__ void dec_load8(DecRegsT<true>& r, const Dec8Src& src,
 }
 
 // Eight E4M3 codes (the lowest byte first) -> eight bf16 / fp32 values.  The
-// conversion is exact: every E4M3 value is a bf16 value, so the upper halves
-// of the fp32 results are the bf16 encodings.
+// conversion is exact: every E4M3 value is a bf16 value.  To bf16: gfx950's
+// scaled pair conversion with scale 1, one instruction per two codes (an
+// in-bounds probe matched it, for every code in each byte position, to the
+// fp32 conversion's upper halves).
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t d0, uint32_t d1) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(d0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(d0, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(d1, false), e = __builtin_amdgcn_cvt_pk_f32_fp8(d1, true);
   u32x4 r;
-  r[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-  r[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
-  r[3] = __builtin_amdgcn_perm(__float_as_uint(e[1]), __float_as_uint(e[0]), 0x07060302u);
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.f, true));
   return __builtin_bit_cast(bf16x8_t, r);
 }
 __device__ __forceinline__ void fp8x8_to_f32(uint32_t d0, uint32_t d1, float v[8]) {
