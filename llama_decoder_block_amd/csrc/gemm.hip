@@ -69,12 +69,18 @@ WRows<T> make_rows(const WSeg& w, int K) {
 // XCD-aware tile order.  Consecutive workgroup ids are dealt round-robin to
 // the 8 XCDs; remapping gives each XCD a contiguous range of the logical
 // order, and the logical order walks GROUP_M row tiles before moving along
-// N so that tiles resident on one XCD share operand panels in its L2.
+// N so that tiles resident on one XCD share operand panels in its L2.  With
+// 4 row tiles (32 resident tiles = 4 x 8 per XCD, 12 distinct panels as with
+// 8 x 4) an XCD's range of the Llama-3-8B prefill products is one group, so
+// all XCDs walk the weight columns in step and share each weight panel
+// through the last-level cache (measured on MI355X against 8: gate/up
+// 1500-1508 -> 1485 us, o 267 -> 255, QKV 363-367 -> 357-360; 2 and 16 were
+// slower than both).
 __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int tiles_n,
                                             int* tm, int* tn) {
   int logical = bid;
   if ((nblk & 7) == 0) logical = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  constexpr int GROUP_M = 8;
+  constexpr int GROUP_M = 4;
   const int group_size = GROUP_M * tiles_n;
   const int group = logical / group_size;
   const int first_m = group * GROUP_M;
