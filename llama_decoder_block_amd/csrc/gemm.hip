@@ -72,7 +72,7 @@ WRows<T> make_rows(const WSeg& w, int K) {
 // N so that tiles resident on one XCD share operand panels in its L2.  With
 // 4 row tiles (32 resident tiles = 4 x 8 per XCD, 12 distinct panels as with
 // 8 x 4) an XCD's range of the Llama-3-8B prefill products is one group, so
-// all XCDs walk the weight columns in step and share each weight panel
+// all XCDs walk the weight columns in step and can share each weight panel
 // through the last-level cache (measured on MI355X against 8: gate/up
 // 1500-1508 -> 1485 us, o 267 -> 255, QKV 363-367 -> 357-360; 2 and 16 were
 // slower than both).
