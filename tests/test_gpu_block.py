@@ -247,17 +247,20 @@ def test_decode_residual_norm_pass(d, n_q, n_kv, batch):
     check_bf16(f"decode d={d} B={batch}", y, inp)
 
 
-def test_decode_qkv_without_k_split():
-    """40 decode rows whose Q/K/V product has too few 64-row weight blocks to
-    fill the GPU but enough 32-row ones (8192 rows: 256 workgroups): the
-    product runs unsplit on 32-row blocks, with the rotation and the cache
-    append in its own epilogue.  Block output and h against both oracles,
-    every row, and the appended cache slot against the oracle's."""
-    wl = synth.workload("llama3_8b_gqa_decode", batch=40, d_model=6144, n_q=48, n_kv=8, head_dim=128,
+@pytest.mark.parametrize("d,n_q,n_kv,batch", [(6144, 48, 8, 40), (4096, 32, 32, 8)])
+def test_decode_qkv_without_k_split(d, n_q, n_kv, batch):
+    """Decode rows whose Q/K/V product has too few 64-row weight blocks to
+    fill the GPU but enough 32-row ones: 40 rows of a GQA product with 8192
+    weight rows (256 workgroups), and 8 rows of a multi-head one with 12288
+    (384 workgroups, the target for at most 32 rows).  The product runs
+    unsplit on 32-row blocks, with the rotation and the cache append in its
+    own epilogue.  Block output and h against both oracles, every row, and
+    the appended cache slot against the oracle's."""
+    wl = synth.workload("llama3_8b_gqa_decode", batch=batch, d_model=d, n_q=n_q, n_kv=n_kv, head_dim=128,
                         d_ff=1536, decode_pos=70, kv_cap=96)
     inp = synth.make_block_inputs(wl)
     y, kc, _ = run_block(inp)
-    check_bf16("decode QKV on 32-row blocks", y, inp)
+    check_bf16(f"decode QKV on 32-row blocks d={d} B={batch}", y, inp)
     _, inter = oracle_block(inp)
     new_k = to64(kc[:, 70])
     assert rel_frobenius(new_k, inter["k_cache"][:, 70]) <= 1e-2
